@@ -1,0 +1,15 @@
+"""Seeded synthetic workloads for AdaLN (no operator arithmetic here)."""
+from .configs import (  # noqa: F401
+    CONFIG_SEEDS,
+    CONFIGS,
+    RAGGED_BUCKETS,
+    RAGGED_D,
+    Problem,
+    ProblemData,
+    algorithmic_bytes,
+    custom_problem,
+    encode_bf16_rne,
+    make_config,
+    make_problem_data,
+    ragged_lengths,
+)

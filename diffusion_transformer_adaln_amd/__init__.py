@@ -1,0 +1,18 @@
+"""Fused AdaLN (LayerNorm + per-sample modulation) for AMD MI355X (gfx950).
+
+The operator runs in hand-written HIP kernels behind the C ABI declared in
+include/adaln.h; this package holds those sources (csrc/), the build step and
+a ctypes binding whose functions carry the C entry points' names.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    AdaLNError,
+    adaln_abi_version,
+    adaln_bwd,
+    adaln_bwd_varlen,
+    adaln_bwd_workspace_size,
+    adaln_fwd,
+    adaln_fwd_varlen,
+    adaln_status_str,
+    load_library,
+)

@@ -1,0 +1,239 @@
+"""ctypes binding of the C ABI in include/adaln.h (argument marshalling only).
+
+Every function here has the name of the C entry point it wraps.  PyTorch
+supplies device memory and the current HIP stream; all computation runs in
+the library's HIP kernels.  If the library is not built the import of this
+module's functions fails loudly: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libadaln.so")
+
+ADALN_F32 = 0
+ADALN_BF16 = 1
+ADALN_OK = 0
+STATUS_NAMES = {
+    0: "ADALN_OK",
+    1: "ADALN_ERR_INVALID_ARG",
+    2: "ADALN_ERR_UNSUPPORTED_DTYPE",
+    3: "ADALN_ERR_UNSUPPORTED_SHAPE",
+    4: "ADALN_ERR_WORKSPACE_TOO_SMALL",
+    5: "ADALN_ERR_ALIASING",
+    6: "ADALN_ERR_HIP",
+}
+
+EXPORTED = (
+    "adaln_fwd",
+    "adaln_bwd",
+    "adaln_fwd_varlen",
+    "adaln_bwd_varlen",
+    "adaln_bwd_workspace_size",
+    "adaln_status_str",
+    "adaln_abi_version",
+)
+
+
+class AdaLNError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)}")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libadaln.so (once).  torch is imported first so that the library
+    binds to the HIP runtime torch already loaded (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m diffusion_transformer_adaln_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    lib.adaln_fwd.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P]
+    lib.adaln_fwd.restype = ctypes.c_int
+    lib.adaln_fwd_varlen.argtypes = [_P, _P, _P, ctypes.c_float, _P, _I64, _I64, _I64, ctypes.c_int, _P,
+                                     _P, _P, _P]
+    lib.adaln_fwd_varlen.restype = ctypes.c_int
+    lib.adaln_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P,
+                              _P, _P, _P]
+    lib.adaln_bwd.restype = ctypes.c_int
+    lib.adaln_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P,
+                                     ctypes.c_size_t, _P, _P, _P, _P]
+    lib.adaln_bwd_varlen.restype = ctypes.c_int
+    lib.adaln_bwd_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
+    lib.adaln_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.adaln_status_str.argtypes = [ctypes.c_int]
+    lib.adaln_status_str.restype = ctypes.c_char_p
+    lib.adaln_abi_version.argtypes = []
+    lib.adaln_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return ADALN_F32
+    if dt == torch.bfloat16:
+        return ADALN_BF16
+    raise TypeError(f"AdaLN supports float32 and bfloat16, got {dt}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("AdaLN tensors must live on a GPU")
+        if not t.is_contiguous():
+            raise ValueError("AdaLN tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("AdaLN tensors must share one device")
+    return dev
+
+
+def _stream(dev, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _raise(fn, st):
+    if st != ADALN_OK:
+        raise AdaLNError(fn, st)
+
+
+# --------------------------------------------------------------------------
+# public functions (names of the C entry points)
+# --------------------------------------------------------------------------
+def adaln_abi_version() -> int:
+    return load_library().adaln_abi_version()
+
+
+def adaln_status_str(status: int) -> str:
+    return load_library().adaln_status_str(int(status)).decode()
+
+
+def adaln_bwd_workspace_size(B: int, total_rows: int, D: int, dtype: torch.dtype, device=None) -> int:
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(lib.adaln_bwd_workspace_size(int(B), int(total_rows), int(D), _dtype_code(dtype)))
+
+
+def adaln_fwd(x, shift, scale, eps: float, y=None, mean=None, rstd=None, stream=None):
+    """Forward of a dense batch: x [B, N, D]; shift, scale [B, D].
+
+    Returns (y [B, N, D], mean [B, N] fp32, rstd [B, N] fp32).
+    """
+    if x.dim() != 3:
+        raise ValueError("adaln_fwd expects x of shape [B, N, D]")
+    B, N, D = x.shape
+    if shift.shape != (B, D) or scale.shape != (B, D):
+        raise ValueError("shift and scale must be [B, D]")
+    if not (x.dtype == shift.dtype == scale.dtype):
+        raise TypeError("x, shift and scale must share a dtype")
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty((B, N), dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty((B, N), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    dev = _check_dev(x, shift, scale, y, mean, rstd)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.adaln_fwd(_ptr(x), _ptr(shift), _ptr(scale), float(eps), B, N, D, _dtype_code(x.dtype),
+                           _stream(dev, stream), _ptr(y), _ptr(mean), _ptr(rstd))
+    _raise("adaln_fwd", st)
+    return y, mean, rstd
+
+
+def adaln_fwd_varlen(x, shift, scale, offsets, eps: float, y=None, mean=None, rstd=None, stream=None):
+    """Forward of packed samples: x [R, D]; shift, scale [B, D]; offsets int64 [B+1] on the device."""
+    if x.dim() != 2:
+        raise ValueError("adaln_fwd_varlen expects x of shape [R, D]")
+    R, D = x.shape
+    B = shift.shape[0]
+    if shift.shape != (B, D) or scale.shape != (B, D) or offsets.shape != (B + 1,):
+        raise ValueError("shift/scale must be [B, D] and offsets [B+1]")
+    if offsets.dtype != torch.int64:
+        raise TypeError("offsets must be int64")
+    y = torch.empty_like(x) if y is None else y
+    mean = torch.empty((R,), dtype=torch.float32, device=x.device) if mean is None else mean
+    rstd = torch.empty((R,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    dev = _check_dev(x, shift, scale, offsets, y, mean, rstd)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.adaln_fwd_varlen(_ptr(x), _ptr(shift), _ptr(scale), float(eps), _ptr(offsets), B, R, D,
+                                  _dtype_code(x.dtype), _stream(dev, stream), _ptr(y), _ptr(mean),
+                                  _ptr(rstd))
+    _raise("adaln_fwd_varlen", st)
+    return y, mean, rstd
+
+
+def _workspace(B, R, D, dtype, dev, workspace):
+    if workspace is None:
+        need = adaln_bwd_workspace_size(B, R, D, dtype, dev)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def adaln_bwd(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, dshift=None, stream=None):
+    """Backward of a dense batch.  Returns (dx [B, N, D], dscale [B, D], dshift [B, D])."""
+    if x.dim() != 3 or dy.shape != x.shape:
+        raise ValueError("adaln_bwd expects dy and x of shape [B, N, D]")
+    B, N, D = x.shape
+    dx = torch.empty_like(x) if dx is None else dx
+    dscale = torch.empty((B, D), dtype=x.dtype, device=x.device) if dscale is None else dscale
+    dshift = torch.empty((B, D), dtype=x.dtype, device=x.device) if dshift is None else dshift
+    dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
+    if mean.dtype != torch.float32 or rstd.dtype != torch.float32:
+        raise TypeError("mean and rstd must be float32")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace)
+        st = lib.adaln_bwd(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
+                           _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream), _ptr(dx),
+                           _ptr(dscale), _ptr(dshift))
+    _raise("adaln_bwd", st)
+    return dx, dscale, dshift
+
+
+def adaln_bwd_varlen(dy, x, scale, mean, rstd, offsets, workspace=None, dx=None, dscale=None, dshift=None,
+                     stream=None):
+    """Backward of packed samples.  Returns (dx [R, D], dscale [B, D], dshift [B, D])."""
+    if x.dim() != 2 or dy.shape != x.shape:
+        raise ValueError("adaln_bwd_varlen expects dy and x of shape [R, D]")
+    R, D = x.shape
+    B = scale.shape[0]
+    if offsets.shape != (B + 1,) or offsets.dtype != torch.int64:
+        raise ValueError("offsets must be int64 [B+1]")
+    dx = torch.empty_like(x) if dx is None else dx
+    dscale = torch.empty((B, D), dtype=x.dtype, device=x.device) if dscale is None else dscale
+    dshift = torch.empty((B, D), dtype=x.dtype, device=x.device) if dshift is None else dshift
+    dev = _check_dev(dy, x, scale, mean, rstd, offsets, dx, dscale, dshift)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace)
+        st = lib.adaln_bwd_varlen(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), _ptr(offsets), B,
+                                  R, D, _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream),
+                                  _ptr(dx), _ptr(dscale), _ptr(dshift))
+    _raise("adaln_bwd_varlen", st)
+    return dx, dscale, dshift

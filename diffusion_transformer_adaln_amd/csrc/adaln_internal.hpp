@@ -1,0 +1,74 @@
+// Internal interface between the host dispatcher (adaln_api.cpp) and the
+// kernel launchers (adaln_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace adaln {
+
+enum DType : int { F32 = 0, BF16 = 1 };
+
+// How rows are grouped into samples.
+//   dense:  sample b owns rows [b*N, (b+1)*N)                 (offsets == nullptr)
+//   varlen: sample b owns rows [offsets[b], offsets[b+1])     (device int64 array)
+struct RowMap {
+  int64_t B;
+  int64_t R;
+  int64_t N;                 // dense rows per sample (unused for varlen)
+  const int64_t* offsets;    // device, B+1 entries, or nullptr for dense
+};
+
+// Backward tiling: every tile is a run of at most `tile_rows` consecutive rows
+// inside one sample.  Sample b's tiles are numbered
+// [tile_start(b), tile_start(b+1)).  Dense: tile_start(b) = b * ceil(N/tile_rows).
+// Varlen: tile_start lives in the workspace and is written by the prologue.
+struct Tiling {
+  int64_t tile_rows;
+  int64_t tiles_max;         // grid size of the row pass (upper bound for varlen)
+  int64_t* tile_start;       // device, B+1 entries (varlen only), else nullptr
+};
+
+// Row layout of the vectorised kernels: a row of D elements is V = D/EPV
+// 16-byte vectors; LPR lanes cooperate on a row, each holding VPT vectors
+// (vector j*LPR + lane).  NT threads per workgroup hold NT/LPR rows at once.
+struct VecPlan {
+  bool ok;
+  int vpt;
+  int lpr;
+  int nt;
+};
+
+// Vector plan for the forward (backward = false) or backward kernels.
+VecPlan plan_vec(int dtype, int64_t D, bool backward);
+
+// Launchers.  Each returns hipSuccess or the launch error.  They assume the
+// arguments were validated by the caller.
+hipError_t launch_fwd(int dtype, const void* x, const void* shift, const void* scale, float eps,
+                      const RowMap& rm, int64_t D, bool vec, const VecPlan& vp, int num_cu,
+                      hipStream_t stream, void* y, float* mean, float* rstd);
+
+hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scale,
+                      const float* mean, const float* rstd, const RowMap& rm, int64_t D,
+                      bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
+                      hipStream_t stream, void* dx, void* dscale, void* dshift);
+
+// Rows per backward tile for R rows on a device with num_cu compute units.
+int64_t bwd_tile_rows(int64_t R, int num_cu);
+
+// Bytes of workspace for the backward (tile table + partial sums).
+size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);
+
+// Layout of that workspace.
+struct WorkspaceLayout {
+  size_t tile_start_off;   // int64 [B+1]
+  size_t partial_off;      // fp32 [tiles_max][2][D]
+  size_t total;
+  int64_t tile_rows;
+  int64_t tiles_max;
+};
+WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
+                                     int64_t N_dense);
+
+}  // namespace adaln

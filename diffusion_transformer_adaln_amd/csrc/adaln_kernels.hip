@@ -1,0 +1,876 @@
+// Fused AdaLN (LayerNorm + per-sample modulation) kernels for gfx950 (CDNA4).
+//
+// The operator is the fused LayerNorm-modulate of the AdaptiveLoad technical
+// summary (gist.science 2605.17923), section 2.B: one launch for the
+// forward with row statistics kept on chip, and a backward whose per-sample
+// modulation gradients are column sums over N taken with threads pinned to
+// feature columns so every access is contiguous along D.
+//
+// The path is HBM-bound (about 2 flop per byte), so nothing here uses MFMA.
+// What matters is bytes in flight, 16-byte vector accesses, and keeping the
+// row in registers between the statistics and the output:
+//
+//   * A row of D elements is V = D/EPV vectors of 16 bytes (EPV = 8 for bf16,
+//     4 for fp32).  LPR lanes (a multiple of 16) cooperate on one row, each
+//     holding VPT vectors: lane l owns vectors l, l+LPR, ..., so each vector
+//     load of a row is one contiguous 16*LPR-byte span.  A workgroup of NT
+//     threads works on NT/LPR rows at a time ("slots"), and each slot keeps
+//     RIF rows in flight per iteration.
+//   * Row reductions run in three fixed-order stages: a 16-lane butterfly
+//     with DPP (quad_perm, row_half_mirror, row_mirror), cross-row lane
+//     exchanges inside the wave, then LDS across the waves or 16-lane groups
+//     that share the row, merged in ascending order by every thread.  Every
+//     lane therefore ends with bitwise identical statistics, and the results
+//     never depend on timing.
+//   * Forward statistics are a parallel (Chan) Welford merge of per-lane
+//     (mean, M2) pairs, so large row offsets and x20 outlier rows lose no
+//     precision.
+//   * The backward keeps each lane's column partial sums of dy and dy*xhat in
+//     registers over a tile of rows inside one sample, combines the slots of a
+//     workgroup through LDS in slot order, and writes them once per tile,
+//     coalesced along D.  A finish kernel adds a sample's tiles in ascending
+//     tile order.  No floating-point atomics anywhere: bitwise repeatable.
+//
+// General kernels (any D, any alignment) cover the shapes the vector layout
+// cannot; they compute the same quantities with scalar accesses.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "adaln_internal.hpp"
+
+namespace adaln {
+
+// ---------------------------------------------------------------------------
+// element helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int DT> struct Elem;
+template <> struct Elem<F32> {
+  static constexpr int EPV = 4;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(f, bf16x2_t);   // v_cvt_pk_bf16_f32: RNE
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+template <> struct Elem<BF16> {
+  static constexpr int EPV = 8;
+  __device__ static __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    unpack2(v.x, f[0], f[1]); unpack2(v.y, f[2], f[3]);
+    unpack2(v.z, f[4], f[5]); unpack2(v.w, f[6], f[7]);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
+  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// cross-lane exchange
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_1032 = 0xB1;       // quad_perm [1,0,3,2]: partner lane ^ 1
+constexpr int DPP_QUAD_2301 = 0x4E;       // quad_perm [2,3,0,1]: partner lane ^ 2
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <-> 7-i inside each 8-lane half row
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <-> 15-i inside each 16-lane row
+
+// Partner value at level k (0..3) of the 16-lane butterfly.  After level k
+// every lane of an aligned group of 2^(k+1) lanes holds that group's result,
+// so any pairing across the two halves completes the next level.
+template <int LEVEL>
+__device__ __forceinline__ float partner16(float v) {
+  if constexpr (LEVEL == 0) return dpp<DPP_QUAD_1032>(v);
+  else if constexpr (LEVEL == 1) return dpp<DPP_QUAD_2301>(v);
+  else if constexpr (LEVEL == 2) return dpp<DPP_ROW_HALF_MIRROR>(v);
+  else return dpp<DPP_ROW_MIRROR>(v);
+}
+
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Chan, Golub and LeVeque's pairwise merge of two (mean, M2) summaries that
+// cover the same count n each (half_n = n/2):
+//   mean = (ma + mb)/2,  M2 = M2a + M2b + (mb - ma)^2 * n/2.
+// Commutative in its two arguments bit for bit, so both partners agree.
+__device__ __forceinline__ void chan_equal(float& m, float& s, float mo, float so, float half_n) {
+  const float d = mo - m;
+  m = 0.5f * (m + mo);
+  s = (s + so) + (d * d) * half_n;
+}
+
+// Merge (mo, so) covering `no` elements into (m, s) covering `n` elements.
+__device__ __forceinline__ void chan_merge(float& m, float& s, float& n, float mo, float so, float no) {
+  const float nt = n + no;
+  const float d = mo - m;
+  const float w = no / nt;
+  m = m + d * w;
+  s = (s + so) + (d * d) * (n * w);
+  n = nt;
+}
+
+// Reduce a (mean, M2) pair over an aligned group of `unit` lanes (16, 32 or
+// 64); n_lane is each lane's element count.  All lanes of the group end with
+// the same bits.
+__device__ __forceinline__ void chan_reduce_unit(float& m, float& s, float n_lane, int unit) {
+  float n = n_lane;
+  float mo, so;
+  mo = partner16<0>(m); so = partner16<0>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<1>(m); so = partner16<1>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<2>(m); so = partner16<2>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<3>(m); so = partner16<3>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  if (unit >= 32) { mo = xor_lane(m, 16); so = xor_lane(s, 16); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f; }
+  if (unit >= 64) { mo = xor_lane(m, 32); so = xor_lane(s, 32); chan_equal(m, s, mo, so, 0.5f * n); }
+}
+
+// Sum over an aligned group of `unit` lanes; all lanes get the same bits.
+__device__ __forceinline__ float sum_unit(float v, int unit) {
+  v = v + partner16<0>(v);
+  v = v + partner16<1>(v);
+  v = v + partner16<2>(v);
+  v = v + partner16<3>(v);
+  if (unit >= 32) v = v + xor_lane(v, 16);
+  if (unit >= 64) v = v + xor_lane(v, 32);
+  return v;
+}
+
+// Lanes that reduce together before LDS: a whole wave when a row covers whole
+// waves, 32 lanes when two rows share a wave, else one 16-lane DPP row.
+__device__ __forceinline__ int reduce_unit(int lpr) {
+  return (lpr % 64 == 0) ? 64 : (lpr == 32 ? 32 : 16);
+}
+
+// ---------------------------------------------------------------------------
+// row -> sample
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t sample_of_row(const RowMap& rm, int64_t row) {
+  if (rm.offsets == nullptr) return row / rm.N;
+  // largest b with offsets[b] <= row  (offsets non-decreasing; empty samples skipped)
+  int64_t lo = 0, hi = rm.B;   // invariant: offsets[lo] <= row < offsets[hi]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (rm.offsets[mid] <= row) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void tile_bounds(const RowMap& rm, const Tiling& tl, int64_t t,
+                                            int64_t& b, int64_t& r0, int64_t& r1) {
+  if (rm.offsets == nullptr) {
+    const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
+    b = t / tps;
+    const int64_t i = t - b * tps;
+    r0 = b * rm.N + i * tl.tile_rows;
+    r1 = b * rm.N + min(rm.N, (i + 1) * tl.tile_rows);
+  } else {
+    // largest b with tile_start[b] <= t
+    int64_t lo = 0, hi = rm.B;
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (tl.tile_start[mid] <= t) lo = mid; else hi = mid;
+    }
+    b = lo;
+    const int64_t i = t - tl.tile_start[b];
+    r0 = rm.offsets[b] + i * tl.tile_rows;
+    r1 = min(rm.offsets[b + 1], r0 + tl.tile_rows);
+  }
+}
+
+// Largest workgroup of the vectorised kernels: 8 waves, i.e. two per SIMD, so
+// the compiler may give each wave up to 256 VGPRs.
+constexpr int VEC_MAX_NT = 512;
+
+// ---------------------------------------------------------------------------
+// vectorised forward
+// ---------------------------------------------------------------------------
+// Grid: one workgroup per chunk of `rows_per_wg` consecutive rows.
+// LDS: 2 buffers x [slots][RIF][groups] x (mean, M2).
+// Rows each slot keeps in flight per iteration: about 8 (forward) or 4
+// (backward, two row arrays) 16-byte vectors per lane, which keeps the
+// kernels clear of register spills at two or more waves per SIMD.
+constexpr int fwd_rif(int vpt) { return vpt <= 1 ? 8 : vpt == 2 ? 4 : vpt <= 4 ? 2 : 1; }
+constexpr int bwd_rif(int vpt) { return vpt <= 1 ? 4 : vpt == 2 ? 2 : 1; }
+constexpr int FWD_MAX_VPT = 8;
+constexpr int BWD_MAX_VPT = 4;
+
+template <int DT, int VPT, int RIF>
+__global__ void __launch_bounds__(VEC_MAX_NT)
+fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
+               const uint4* __restrict__ scale, float eps, RowMap rm, int V, int D, int lpr,
+               int64_t rows_per_wg, uint4* __restrict__ y, float* __restrict__ mean,
+               float* __restrict__ rstd) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::EPV;
+  extern __shared__ float2 lds_f2[];
+
+  const int tid = threadIdx.x;
+  const int nslots = blockDim.x / lpr;
+  const int slot = tid / lpr;
+  const int lane = tid - slot * lpr;
+  const int unit = reduce_unit(lpr);
+  const int groups = lpr / unit;          // LDS partials per row
+  const int group = lane / unit;
+  const bool leader = (lane % unit) == 0;
+  const int buf_stride = nslots * RIF * groups;
+
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t r_end = min(rm.R, r_begin + rows_per_wg);
+  const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
+  const float inv_d = 1.0f / static_cast<float>(D);
+  constexpr float n_lane = static_cast<float>(VPT * EPV);
+
+  float sc1[VPT][EPV], sh[VPT][EPV];
+  int64_t cur_b = -1;
+  int it = 0;
+
+  for (int64_t base = r_begin; base < r_end; base += rows_per_iter, ++it) {
+    uint4 xv[RIF][VPT];
+    int64_t row[RIF];
+    bool valid[RIF];
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      row[i] = base + static_cast<int64_t>(slot) * RIF + i;
+      valid[i] = row[i] < r_end;
+      const uint4* xr = x + row[i] * V + lane;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) xv[i][j] = valid[i] ? xr[j * lpr] : make_uint4(0, 0, 0, 0);
+    }
+
+    // per-lane two-pass (mean, M2), then the fixed-order merge across lanes
+    float m[RIF], s[RIF];
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        float f[EPV];
+        E::unpack(xv[i][j], f);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) acc += f[k];
+      }
+      const float ml = acc * (1.0f / n_lane);
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        float f[EPV];
+        E::unpack(xv[i][j], f);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) { const float d = f[k] - ml; sq += d * d; }
+      }
+      m[i] = ml; s[i] = sq;
+      chan_reduce_unit(m[i], s[i], n_lane, unit);
+    }
+    if (groups > 1) {
+      float2* buf = lds_f2 + (it & 1) * buf_stride;
+      if (leader) {
+#pragma unroll
+        for (int i = 0; i < RIF; ++i) buf[(slot * RIF + i) * groups + group] = make_float2(m[i], s[i]);
+      }
+      __syncthreads();
+      const float n_unit = n_lane * static_cast<float>(unit);
+#pragma unroll
+      for (int i = 0; i < RIF; ++i) {
+        const float2* p = buf + (slot * RIF + i) * groups;
+        float2 v = p[0];
+        float mm = v.x, ss = v.y, nn = n_unit;
+        for (int g = 1; g < groups; ++g) { v = p[g]; chan_merge(mm, ss, nn, v.x, v.y, n_unit); }
+        m[i] = mm; s[i] = ss;
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      if (!valid[i]) continue;
+      const float rs = 1.0f / sqrtf(s[i] * inv_d + eps);
+      if (lane == 0) { mean[row[i]] = m[i]; rstd[row[i]] = rs; }
+      const int64_t b = sample_of_row(rm, row[i]);
+      if (b != cur_b) {
+        cur_b = b;
+        const uint4* scp = scale + b * V + lane;
+        const uint4* shp = shift + b * V + lane;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          E::unpack(scp[j * lpr], sc1[j]);
+          E::unpack(shp[j * lpr], sh[j]);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
+        }
+      }
+      uint4* yr = y + row[i] * V + lane;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        float f[EPV];
+        E::unpack(xv[i][j], f);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float xh = (f[k] - m[i]) * rs;      // (x - mean) * rstd
+          f[k] = xh * sc1[j][k] + sh[j][k];
+        }
+        yr[j * lpr] = E::pack(f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// vectorised backward row pass
+// ---------------------------------------------------------------------------
+// Grid: one workgroup per tile (a run of rows inside one sample).
+// LDS: 2 buffers x [slots][RIF][groups] x (sum g, sum g*xhat), then, when a
+// workgroup holds several slots, [2][D] floats for the slot combine.
+template <int DT, int VPT, int RIF>
+__global__ void __launch_bounds__(VEC_MAX_NT)
+bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
+               const uint4* __restrict__ scale, const float* __restrict__ mean,
+               const float* __restrict__ rstd, RowMap rm, Tiling tl, int V, int D, int lpr,
+               float* __restrict__ partial, uint4* __restrict__ dx) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::EPV;
+  extern __shared__ float2 lds_f2[];
+
+  const int64_t t = blockIdx.x;
+  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
+  int64_t b, r0, r1;
+  tile_bounds(rm, tl, t, b, r0, r1);
+
+  const int tid = threadIdx.x;
+  const int nslots = blockDim.x / lpr;
+  const int slot = tid / lpr;
+  const int lane = tid - slot * lpr;
+  const int unit = reduce_unit(lpr);
+  const int groups = lpr / unit;
+  const int group = lane / unit;
+  const bool leader = (lane % unit) == 0;
+  const int buf_stride = nslots * RIF * groups;
+  const float inv_d = 1.0f / static_cast<float>(D);
+
+  float sc1[VPT][EPV];
+  {
+    const uint4* scp = scale + b * V + lane;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      E::unpack(scp[j * lpr], sc1[j]);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
+    }
+  }
+  float acc_h[VPT][EPV], acc_s[VPT][EPV];   // column partials of dy and dy*xhat
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) { acc_h[j][k] = 0.f; acc_s[j][k] = 0.f; }
+
+  const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
+  int it = 0;
+  for (int64_t base = r0; base < r1; base += rows_per_iter, ++it) {
+    uint4 xv[RIF][VPT], gv[RIF][VPT];
+    int64_t row[RIF];
+    bool valid[RIF];
+    float mu[RIF], rs[RIF];
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      row[i] = base + static_cast<int64_t>(slot) * RIF + i;
+      valid[i] = row[i] < r1;
+      const int64_t rr = valid[i] ? row[i] : r0;
+      mu[i] = mean[rr];
+      rs[i] = rstd[rr];
+      const uint4* xr = x + rr * V + lane;
+      const uint4* gr = dy + rr * V + lane;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) { xv[i][j] = xr[j * lpr]; gv[i][j] = gr[j * lpr]; }
+    }
+
+    float sg[RIF], sgx[RIF];
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      float a = 0.f, c = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        float fx[EPV], fg[EPV];
+        E::unpack(xv[i][j], fx);
+        E::unpack(gv[i][j], fg);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float xh = (fx[k] - mu[i]) * rs[i];
+          const float g = fg[k] * sc1[j][k];
+          a += g;
+          c += g * xh;
+        }
+      }
+      sg[i] = sum_unit(a, unit);
+      sgx[i] = sum_unit(c, unit);
+    }
+    if (groups > 1) {
+      float2* buf = lds_f2 + (it & 1) * buf_stride;
+      if (leader) {
+#pragma unroll
+        for (int i = 0; i < RIF; ++i) buf[(slot * RIF + i) * groups + group] = make_float2(sg[i], sgx[i]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < RIF; ++i) {
+        const float2* p = buf + (slot * RIF + i) * groups;
+        float2 v = p[0];
+        float a = v.x, c = v.y;
+        for (int g = 1; g < groups; ++g) { v = p[g]; a += v.x; c += v.y; }
+        sg[i] = a; sgx[i] = c;
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < RIF; ++i) {
+      if (!valid[i]) continue;
+      const float a = sg[i] * inv_d, c = sgx[i] * inv_d;
+      uint4* dxr = dx + row[i] * V + lane;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        float fx[EPV], fg[EPV], out[EPV];
+        E::unpack(xv[i][j], fx);
+        E::unpack(gv[i][j], fg);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float xh = (fx[k] - mu[i]) * rs[i];
+          const float g = fg[k] * sc1[j][k];
+          out[k] = rs[i] * ((g - a) - xh * c);
+          acc_h[j][k] += fg[k];
+          acc_s[j][k] += fg[k] * xh;
+        }
+        dxr[j * lpr] = E::pack(out);
+      }
+    }
+  }
+
+  // tile partials: partial[t][0][:] = sum dy, partial[t][1][:] = sum dy*xhat
+  float* ph = partial + t * 2 * static_cast<int64_t>(D);
+  float* ps = ph + D;
+  if (nslots == 1) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int col = (j * lpr + lane) * EPV;
+#pragma unroll
+      for (int k = 0; k < EPV; k += 4) {
+        *reinterpret_cast<float4*>(ph + col + k) = make_float4(acc_h[j][k], acc_h[j][k + 1], acc_h[j][k + 2], acc_h[j][k + 3]);
+        *reinterpret_cast<float4*>(ps + col + k) = make_float4(acc_s[j][k], acc_s[j][k + 1], acc_s[j][k + 2], acc_s[j][k + 3]);
+      }
+    }
+  } else {
+    float* comb = reinterpret_cast<float*>(lds_f2 + 2 * buf_stride);   // [2][D]
+    __syncthreads();
+    for (int sl = 0; sl < nslots; ++sl) {
+      if (slot == sl) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          const int col = (j * lpr + lane) * EPV;
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) {
+            if (sl == 0) { comb[col + k] = acc_h[j][k]; comb[D + col + k] = acc_s[j][k]; }
+            else { comb[col + k] += acc_h[j][k]; comb[D + col + k] += acc_s[j][k]; }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    for (int c = tid * 4; c < 2 * D; c += blockDim.x * 4)
+      *reinterpret_cast<float4*>(ph + c) = *reinterpret_cast<const float4*>(comb + c);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// general kernels (any D, any alignment): scalar accesses, re-reads from cache
+// ---------------------------------------------------------------------------
+constexpr int GEN_NT = 256;
+
+// Sum over the workgroup in a fixed order; every thread returns the same bits.
+// `red` holds GEN_NT/64 floats; the caller alternates between two buffers.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = sum_unit(v, 64);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int i = 1; i < GEN_NT / 64; ++i) s += red[i];
+  return s;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(GEN_NT)
+fwd_gen_kernel(const void* __restrict__ x, const void* __restrict__ shift,
+               const void* __restrict__ scale, float eps, RowMap rm, int D,
+               int64_t rows_per_wg, void* __restrict__ y, float* __restrict__ mean,
+               float* __restrict__ rstd) {
+  using E = Elem<DT>;
+  __shared__ float red[4][GEN_NT / 64];
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  const int64_t r_end = min(rm.R, r_begin + rows_per_wg);
+  int k = 0;
+  for (int64_t r = r_begin; r < r_end; ++r) {
+    const int64_t base = r * D;
+    float a = 0.f;
+    for (int d = threadIdx.x; d < D; d += GEN_NT) a += E::load1(x, base + d);
+    const float mu = block_sum(a, red[(k++) & 3]) / static_cast<float>(D);
+    float q = 0.f;
+    for (int d = threadIdx.x; d < D; d += GEN_NT) { const float t = E::load1(x, base + d) - mu; q += t * t; }
+    const float var = block_sum(q, red[(k++) & 3]) / static_cast<float>(D);
+    const float rs = 1.0f / sqrtf(var + eps);
+    if (threadIdx.x == 0) { mean[r] = mu; rstd[r] = rs; }
+    const int64_t b = sample_of_row(rm, r);
+    for (int d = threadIdx.x; d < D; d += GEN_NT) {
+      const float xh = (E::load1(x, base + d) - mu) * rs;
+      E::store1(y, base + d, xh * (1.0f + E::load1(scale, b * D + d)) + E::load1(shift, b * D + d));
+    }
+  }
+}
+
+// One workgroup per tile; column partials accumulate in the tile's slice of
+// `partial`, each column owned by one thread for the whole tile.
+template <int DT>
+__global__ void __launch_bounds__(GEN_NT)
+bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
+               const void* __restrict__ scale, const float* __restrict__ mean,
+               const float* __restrict__ rstd, RowMap rm, Tiling tl, int D,
+               float* __restrict__ partial, void* __restrict__ dx) {
+  using E = Elem<DT>;
+  __shared__ float red[4][GEN_NT / 64];
+  const int64_t t = blockIdx.x;
+  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;
+  int64_t b, r0, r1;
+  tile_bounds(rm, tl, t, b, r0, r1);
+  float* ph = partial + t * 2 * static_cast<int64_t>(D);
+  float* ps = ph + D;
+  for (int d = threadIdx.x; d < D; d += GEN_NT) { ph[d] = 0.f; ps[d] = 0.f; }
+  const float inv_d = 1.0f / static_cast<float>(D);
+  int k = 0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t base = r * D;
+    const float mu = mean[r], rs = rstd[r];
+    float a = 0.f, c = 0.f;
+    for (int d = threadIdx.x; d < D; d += GEN_NT) {
+      const float xh = (E::load1(x, base + d) - mu) * rs;
+      const float g = E::load1(dy, base + d) * (1.0f + E::load1(scale, b * D + d));
+      a += g; c += g * xh;
+    }
+    a = block_sum(a, red[(k++) & 3]) * inv_d;
+    c = block_sum(c, red[(k++) & 3]) * inv_d;
+    for (int d = threadIdx.x; d < D; d += GEN_NT) {
+      const float xh = (E::load1(x, base + d) - mu) * rs;
+      const float gy = E::load1(dy, base + d);
+      const float g = gy * (1.0f + E::load1(scale, b * D + d));
+      E::store1(dx, base + d, rs * ((g - a) - xh * c));
+      ph[d] += gy;
+      ps[d] += gy * xh;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
+// ---------------------------------------------------------------------------
+// Workgroup = FIN_COLS column lanes x FIN_SLICES tile slices.  Slice k adds
+// tiles k, k+FIN_SLICES, ... in ascending order; the slices are then added in
+// ascending slice order through LDS.  The grouping depends only on the tile
+// count, so the result is the same on every run.
+constexpr int FIN_COLS = 64;
+constexpr int FIN_SLICES = 4;
+
+template <int DT>
+__global__ void __launch_bounds__(FIN_COLS * FIN_SLICES)
+finish_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks,
+              void* __restrict__ dscale, void* __restrict__ dshift) {
+  using E = Elem<DT>;
+  __shared__ float sh_h[FIN_SLICES][FIN_COLS];
+  __shared__ float sh_s[FIN_SLICES][FIN_COLS];
+  const int64_t b = blockIdx.x / col_blocks;
+  const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
+  const int lane = threadIdx.x % FIN_COLS;
+  const int slice = threadIdx.x / FIN_COLS;
+  const int d = cb * FIN_COLS + lane;
+
+  int64_t t0, t1;
+  if (rm.offsets == nullptr) {
+    const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
+    t0 = b * tps; t1 = t0 + tps;
+  } else {
+    t0 = tl.tile_start[b]; t1 = tl.tile_start[b + 1];
+  }
+  float h = 0.f, s = 0.f;
+  if (d < D) {
+    const int64_t stride = 2 * static_cast<int64_t>(D);
+    for (int64_t t = t0 + slice; t < t1; t += FIN_SLICES) {
+      h += partial[t * stride + d];
+      s += partial[t * stride + D + d];
+    }
+  }
+  sh_h[slice][lane] = h;
+  sh_s[slice][lane] = s;
+  __syncthreads();
+  if (slice == 0 && d < D) {
+    float hh = sh_h[0][lane], ss = sh_s[0][lane];
+#pragma unroll
+    for (int k = 1; k < FIN_SLICES; ++k) { hh += sh_h[k][lane]; ss += sh_s[k][lane]; }
+    E::store1(dshift, b * D + d, hh);
+    E::store1(dscale, b * D + d, ss);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// varlen prologue: tile_start[b] = sum_{c<b} ceil(rows_c / tile_rows)
+// ---------------------------------------------------------------------------
+constexpr int PRO_NT = 1024;
+
+__global__ void __launch_bounds__(PRO_NT)
+varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile_rows,
+                    int64_t* __restrict__ tile_start) {
+  __shared__ int64_t scan[PRO_NT];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < B; base += PRO_NT) {
+    const int64_t b = base + threadIdx.x;
+    int64_t cnt = 0;
+    if (b < B) {
+      const int64_t n = offsets[b + 1] - offsets[b];
+      cnt = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
+    }
+    scan[threadIdx.x] = cnt;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the chunk
+    for (int off = 1; off < PRO_NT; off <<= 1) {
+      const int64_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (b < B) tile_start[b] = carry + scan[threadIdx.x] - cnt;   // exclusive
+    __syncthreads();
+    if (threadIdx.x == PRO_NT - 1) carry += scan[PRO_NT - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tile_start[B] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// plans and launchers
+// ---------------------------------------------------------------------------
+// Vector counts per lane tried in order; the first that gives a lane count
+// that is a multiple of 16 (and at most 1024) wins, preferring whole waves.
+static const int kVptOrderBf16[] = {2, 3, 4, 1, 5, 6, 8, 7};
+static const int kVptOrderF32[] = {2, 4, 3, 1, 5, 6, 8, 7};
+
+// Dynamic LDS of a vectorised launch: double-buffered per-row reduction
+// partials, plus the [2][D] slot-combine buffer of a multi-slot backward.
+static size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
+  const int nslots = p.nt / p.lpr;
+  const int unit = (p.lpr % 64 == 0) ? 64 : (p.lpr == 32 ? 32 : 16);
+  const int groups = p.lpr / unit;
+  const int rif = backward ? bwd_rif(p.vpt) : fwd_rif(p.vpt);
+  size_t b = groups > 1 || backward ? 2 * static_cast<size_t>(nslots) * rif * groups * sizeof(float2) : 0;
+  if (backward && nslots > 1) b += 2 * static_cast<size_t>(D) * sizeof(float);
+  return b;
+}
+
+VecPlan plan_vec(int dtype, int64_t D, bool backward) {
+  VecPlan p{false, 0, 0, 0};
+  const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
+  const int epv = dtype == BF16 ? 8 : 4;
+  if (D <= 0 || D % epv != 0) return p;
+  const int64_t V = D / epv;
+  const int* order = dtype == BF16 ? kVptOrderBf16 : kVptOrderF32;
+  for (int pass = 0; pass < 2 && !p.ok; ++pass) {
+    for (int i = 0; i < 8; ++i) {
+      const int vpt = order[i];
+      if (vpt > max_vpt || V % vpt) continue;
+      const int64_t lpr = V / vpt;
+      if (lpr % 16 || lpr > VEC_MAX_NT) continue;
+      if (pass == 0 && lpr % 64) continue;     // first pass: whole waves only
+      p.ok = true; p.vpt = vpt; p.lpr = static_cast<int>(lpr);
+      break;
+    }
+  }
+  if (!p.ok) return p;
+  // threads per workgroup: a multiple of both the row lanes and the wave,
+  // grown to at least 256 threads when the rows are short
+  int nt = p.lpr;
+  while (nt % 64) nt += p.lpr;
+  while (nt < 256 && nt * 2 <= VEC_MAX_NT) nt *= 2;
+  if (nt > VEC_MAX_NT) { p.ok = false; return p; }
+  p.nt = nt;
+  if (vec_lds_bytes(p, D, backward) > 65536) p.ok = false;
+  return p;
+}
+
+constexpr int BWD_TILES_PER_CU = 2;
+constexpr int FWD_WG_PER_CU = 4;
+
+int64_t bwd_tile_rows(int64_t R, int num_cu) {
+  const int64_t target = static_cast<int64_t>(num_cu) * BWD_TILES_PER_CU;
+  return R <= 0 ? 1 : (R + target - 1) / target;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
+                                     int64_t N_dense) {
+  WorkspaceLayout w{};
+  w.tile_rows = bwd_tile_rows(R, num_cu);
+  const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;
+  if (varlen) w.tiles_max = bound;
+  else w.tiles_max = B * ((N_dense + w.tile_rows - 1) / w.tile_rows);
+  w.tile_start_off = 0;
+  w.partial_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
+  w.total = w.partial_off + static_cast<size_t>(bound) * 2 * static_cast<size_t>(D) * sizeof(float);
+  return w;
+}
+
+size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu) {
+  return bwd_workspace_layout(B, R, D, num_cu, true, 0).total;
+}
+
+template <int DT, int VPT>
+static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* scale, float eps,
+                                 const RowMap& rm, int64_t D, const VecPlan& vp, int num_cu,
+                                 hipStream_t stream, void* y, float* mean, float* rstd) {
+  constexpr int EPV = Elem<DT>::EPV;
+  constexpr int RIF = fwd_rif(VPT);
+  const int V = static_cast<int>(D / EPV);
+  const int nslots = vp.nt / vp.lpr;
+  const size_t lds = vec_lds_bytes(vp, D, false);
+  const int64_t per_iter = static_cast<int64_t>(nslots) * RIF;
+  const int64_t target = static_cast<int64_t>(num_cu) * FWD_WG_PER_CU;
+  int64_t rows_per_wg = (rm.R + target - 1) / target;
+  rows_per_wg = ((rows_per_wg + per_iter - 1) / per_iter) * per_iter;
+  const int64_t grid = (rm.R + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((fwd_vec_kernel<DT, VPT, RIF>), dim3(static_cast<unsigned>(grid)),
+                     dim3(vp.nt), lds, stream, static_cast<const uint4*>(x),
+                     static_cast<const uint4*>(shift), static_cast<const uint4*>(scale), eps, rm, V,
+                     static_cast<int>(D), vp.lpr, rows_per_wg, static_cast<uint4*>(y), mean, rstd);
+  return hipGetLastError();
+}
+
+template <int DT, int VPT>
+static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd, const RowMap& rm,
+                                 int64_t D, const VecPlan& vp, const Tiling& tl, float* partial,
+                                 hipStream_t stream, void* dx) {
+  constexpr int EPV = Elem<DT>::EPV;
+  constexpr int RIF = bwd_rif(VPT);
+  const int V = static_cast<int>(D / EPV);
+  const size_t lds = vec_lds_bytes(vp, D, true);
+  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF>), dim3(static_cast<unsigned>(tl.tiles_max)),
+                     dim3(vp.nt), lds, stream, static_cast<const uint4*>(dy),
+                     static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
+                     tl, V, static_cast<int>(D), vp.lpr, partial, static_cast<uint4*>(dx));
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t fwd_dispatch(const void* x, const void* shift, const void* scale, float eps,
+                               const RowMap& rm, int64_t D, bool vec, const VecPlan& vp,
+                               int num_cu, hipStream_t stream, void* y, float* mean, float* rstd) {
+  if (vec) {
+    switch (vp.vpt) {
+      case 1: return fwd_vec_launch<DT, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 2: return fwd_vec_launch<DT, 2>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 3: return fwd_vec_launch<DT, 3>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 4: return fwd_vec_launch<DT, 4>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 5: return fwd_vec_launch<DT, 5>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 6: return fwd_vec_launch<DT, 6>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 7: return fwd_vec_launch<DT, 7>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 8: return fwd_vec_launch<DT, 8>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const int64_t target = static_cast<int64_t>(num_cu) * 8;
+  const int64_t rows_per_wg = (rm.R + target - 1) / target;
+  const int64_t grid = (rm.R + rows_per_wg - 1) / rows_per_wg;
+  hipLaunchKernelGGL((fwd_gen_kernel<DT>), dim3(static_cast<unsigned>(grid)), dim3(GEN_NT), 0,
+                     stream, x, shift, scale, eps, rm, static_cast<int>(D), rows_per_wg, y, mean,
+                     rstd);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
+                               const float* mean, const float* rstd, const RowMap& rm, int64_t D,
+                               bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
+                               hipStream_t stream, void* dx, void* dscale, void* dshift) {
+  hipError_t e = hipSuccess;
+  if (rm.offsets != nullptr) {
+    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
+                       tl.tile_rows, tl.tile_start);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (rm.R > 0 && tl.tiles_max > 0) {
+    if (vec) {
+      switch (vp.vpt) {
+        case 1: e = bwd_vec_launch<DT, 1>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+        case 2: e = bwd_vec_launch<DT, 2>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+        case 3: e = bwd_vec_launch<DT, 3>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+        case 4: e = bwd_vec_launch<DT, 4>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_gen_kernel<DT>), dim3(static_cast<unsigned>(tl.tiles_max)),
+                         dim3(GEN_NT), 0, stream, dy, x, scale, mean, rstd, rm, tl,
+                         static_cast<int>(D), partial, dx);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+  }
+  const int col_blocks = static_cast<int>((D + FIN_COLS - 1) / FIN_COLS);
+  const int64_t grid = rm.B * col_blocks;
+  hipLaunchKernelGGL((finish_kernel<DT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(FIN_COLS * FIN_SLICES), 0, stream, partial, rm, tl, static_cast<int>(D),
+                     col_blocks, dscale, dshift);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(int dtype, const void* x, const void* shift, const void* scale, float eps,
+                      const RowMap& rm, int64_t D, bool vec, const VecPlan& vp, int num_cu,
+                      hipStream_t stream, void* y, float* mean, float* rstd) {
+  if (rm.R == 0) return hipSuccess;
+  return dtype == BF16
+             ? fwd_dispatch<BF16>(x, shift, scale, eps, rm, D, vec, vp, num_cu, stream, y, mean, rstd)
+             : fwd_dispatch<F32>(x, shift, scale, eps, rm, D, vec, vp, num_cu, stream, y, mean, rstd);
+}
+
+hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scale,
+                      const float* mean, const float* rstd, const RowMap& rm, int64_t D,
+                      bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
+                      hipStream_t stream, void* dx, void* dscale, void* dshift) {
+  return dtype == BF16
+             ? bwd_dispatch<BF16>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift)
+             : bwd_dispatch<F32>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift);
+}
+
+}  // namespace adaln

@@ -1,0 +1,187 @@
+/*
+ * adaln.h -- C ABI of the fused adaptive-LayerNorm (AdaLN) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the fused LayerNorm-modulate of the AdaptiveLoad technical
+ * summary (gist.science, paper 2605.17923), section 2.B "Kernels CUDA
+ * Fusionados LayerNorm-Modulate": normalisation and modulation in one launch
+ * with the row statistics kept on chip (forward bullet), and a backward whose
+ * per-sample modulation gradients are sums over the sequence axis N computed
+ * with threads pinned to a feature index d so that memory accesses stay
+ * contiguous along D (backward bullet, "Reducción Coalescida D-tile").  The
+ * summary prints no formula; the operator is the plain chain it fuses:
+ *
+ *   forward, row r of sample b, D features, fp32 statistics:
+ *     mean_r = sum_d x[r,d] / D
+ *     rstd_r = 1 / sqrt( sum_d (x[r,d] - mean_r)^2 / D + eps )
+ *     xhat   = (x - mean_r) * rstd_r
+ *     y      = xhat * (1 + scale[b,:]) + shift[b,:]
+ *   backward:
+ *     g      = dy * (1 + scale[b,:])
+ *     dx     = rstd_r * ( g - mean_d(g) - xhat * mean_d(g * xhat) )
+ *     dscale[b,d] = sum over rows of sample b of dy * xhat
+ *     dshift[b,d] = sum over rows of sample b of dy
+ *
+ * Layout.  Every tensor is contiguous and row-major with D innermost:
+ * x, y, dy, dx are [R, D] (R token rows; a dense batch is [B, N, D] with
+ * R = B*N); shift, scale, dscale, dshift are [B, D]; mean and rstd are fp32
+ * [R].  x, y, dy, dx, shift, scale, dscale, dshift all have the element type
+ * `dtype`; statistics and every accumulation are fp32; bf16 results are
+ * rounded to nearest, ties to even, once.
+ *
+ * Ownership.  Every pointer is a device pointer owned by the caller; the
+ * library never allocates, frees or synchronises, and keeps no state except
+ * a per-device cache of device properties filled on first use.  Every call
+ * is enqueued asynchronously on `stream` (NULL = the null stream) and returns
+ * as soon as its kernels are enqueued.  Calls on different streams may run
+ * concurrently as long as their buffers are disjoint.
+ *
+ * Errors.  The return code is the only error channel; no exception crosses
+ * the ABI.  All arguments are validated before any kernel is enqueued, so a
+ * non-OK return from validation means nothing was launched and no output was
+ * written.  Only the first failing check is reported.  ADALN_ERR_HIP means a
+ * HIP call failed (device query or launch); outputs are then unspecified.
+ *
+ * Determinism.  For the same inputs, shape, dtype and device, every output is
+ * bitwise identical from run to run: every reduction, including the
+ * two-stage column reduction behind dscale and dshift, has a fixed order and
+ * no floating-point atomics are used.
+ *
+ * Performance paths.  Rows whose byte length is a multiple of 16 and whose
+ * pointers are 16-byte aligned, with D/(elements per 16 bytes) divisible into
+ * 16-lane groups, run the vectorised register-resident kernels; every other
+ * shape runs a general (slower, equally exact) kernel.  Both meet the same
+ * tolerances.
+ */
+#ifndef ADALN_H_
+#define ADALN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADALN_ABI_VERSION 1
+
+/* Element type of x, y, dy, dx, shift, scale, dscale, dshift. */
+typedef enum {
+  ADALN_F32 = 0,  /* IEEE binary32 */
+  ADALN_BF16 = 1  /* bfloat16: the upper half of a binary32 */
+} adaln_dtype_t;
+
+typedef enum {
+  ADALN_OK = 0,
+  ADALN_ERR_INVALID_ARG = 1,        /* null pointer, negative size, bad eps, bad offsets */
+  ADALN_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype is not one of adaln_dtype_t */
+  ADALN_ERR_UNSUPPORTED_SHAPE = 3,  /* D above ADALN_MAX_D, or sizes that overflow int64 bytes */
+  ADALN_ERR_WORKSPACE_TOO_SMALL = 4,/* backward workspace smaller than adaln_bwd_workspace_size() */
+  ADALN_ERR_ALIASING = 5,           /* an output overlaps an input or another output */
+  ADALN_ERR_HIP = 6                 /* a HIP runtime call or kernel launch failed */
+} adaln_status_t;
+
+/* Largest supported feature dimension. */
+#define ADALN_MAX_D 65536
+
+/*
+ * adaln_fwd -- forward of a dense batch [B, N, D].
+ *
+ *   x      [B*N, D]  dtype   input token rows
+ *   shift  [B, D]    dtype   per-sample shift
+ *   scale  [B, D]    dtype   per-sample scale (rows are multiplied by 1 + scale)
+ *   eps              float   added to the biased variance inside the square root;
+ *                            finite and >= 0
+ *   B >= 1, N >= 0, 1 <= D <= ADALN_MAX_D
+ *   y      [B*N, D]  dtype   output; must not overlap any input
+ *   mean   [B*N]     fp32    saved row means (for adaln_bwd)
+ *   rstd   [B*N]     fp32    saved 1/sqrt(var + eps)
+ *
+ * N == 0 is a valid empty call: nothing is launched.
+ * One kernel launch.  Section 2.B, forward bullet.
+ */
+adaln_status_t adaln_fwd(const void* x, const void* shift, const void* scale, float eps,
+                         int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
+                         hipStream_t stream, void* y, float* mean, float* rstd);
+
+/*
+ * adaln_bwd_workspace_size -- bytes of device workspace adaln_bwd and
+ * adaln_bwd_varlen need for B samples, total_rows rows and D features on the
+ * current device.  Returns 0 for invalid sizes.  The size depends on the
+ * device's compute-unit count; query it on the device that will run the call.
+ */
+size_t adaln_bwd_workspace_size(int64_t B, int64_t total_rows, int64_t D, adaln_dtype_t dtype);
+
+/*
+ * adaln_bwd -- backward of a dense batch [B, N, D].
+ *
+ *   dy     [B*N, D]  dtype   upstream gradient of y
+ *   x      [B*N, D]  dtype   the forward's input
+ *   scale  [B, D]    dtype   the forward's scale
+ *   mean, rstd [B*N] fp32    the statistics adaln_fwd saved for this x and eps
+ *   B, N, D                  as in adaln_fwd
+ *   workspace        device scratch of at least adaln_bwd_workspace_size(B, B*N, D, dtype)
+ *                    bytes, 16-byte aligned, owned by the caller; its contents
+ *                    on entry are ignored and on exit are unspecified
+ *   dx     [B*N, D]  dtype   gradient of x
+ *   dscale [B, D]    dtype   gradient of scale: sum over the sample's rows of dy * xhat
+ *   dshift [B, D]    dtype   gradient of shift: sum over the sample's rows of dy
+ *
+ * Outputs must not overlap inputs, each other or the workspace.  With N == 0
+ * the call writes zeros to dscale and dshift.  Two launches: a fused row pass
+ * (dx plus per-tile column partial sums kept along D) and a deterministic
+ * finish that adds each sample's tile partials in ascending tile order.
+ * Section 2.B, backward bullet.
+ */
+adaln_status_t adaln_bwd(const void* dy, const void* x, const void* scale,
+                         const float* mean, const float* rstd,
+                         int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         void* dx, void* dscale, void* dshift);
+
+/*
+ * adaln_fwd_varlen -- forward of B samples packed back to back.
+ *
+ *   offsets_dev [B+1] int64, DEVICE memory: sample b owns rows
+ *                    offsets[b] .. offsets[b+1]-1; offsets[0] = 0,
+ *                    offsets[B] = total_rows, non-decreasing.  The host
+ *                    cannot read device memory without synchronising, so
+ *                    these values are trusted: only B and total_rows are
+ *                    validated.
+ *   other arguments as in adaln_fwd with R = total_rows >= 0.
+ *
+ * Samples may have zero rows.  One kernel launch; each row finds its sample
+ * by binary search over the offsets.
+ */
+adaln_status_t adaln_fwd_varlen(const void* x, const void* shift, const void* scale, float eps,
+                                const int64_t* offsets_dev, int64_t B, int64_t total_rows,
+                                int64_t D, adaln_dtype_t dtype, hipStream_t stream,
+                                void* y, float* mean, float* rstd);
+
+/*
+ * adaln_bwd_varlen -- backward of B packed samples (offsets as in
+ * adaln_fwd_varlen).  Three launches: a one-workgroup prologue that turns
+ * the offsets into a table of row tiles (each inside one sample) in the
+ * workspace, the fused row pass, and the deterministic finish.  A sample
+ * with zero rows gets zero dscale and dshift.
+ */
+adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale,
+                                const float* mean, const float* rstd,
+                                const int64_t* offsets_dev, int64_t B, int64_t total_rows,
+                                int64_t D, adaln_dtype_t dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                void* dx, void* dscale, void* dshift);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* adaln_status_str(adaln_status_t status);
+
+/* ADALN_ABI_VERSION of the built library. */
+int adaln_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADALN_H_ */

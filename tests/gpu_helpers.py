@@ -1,0 +1,199 @@
+"""Shared helpers for the GPU tests: upload seeded inputs, run the HIP path
+through the C ABI binding, and compare with the fp64 oracle.
+
+Tolerances (the operator's accuracy contract):
+  fp32 I/O: max abs error 1e-4 on y and dx; max relative error 1e-4 on
+            dscale and dshift
+  bf16 I/O: max abs error 2e-2 on y and dx; max relative error 1e-2 on
+            dscale and dshift
+The relative error of a column sum uses max(|ref|, 1e-3 * rms(ref of that
+sample)) as denominator, so sums that cancel to nearly zero are judged on
+the scale of their sample (an fp32 sum's absolute error does not shrink with
+its value).  Two stricter internal gates are applied as well:
+normwise error max|got-ref| / max|ref| of y and dx at most 1e-2 (bf16) or
+1e-5 (fp32), and fp32 statistics (mean, rstd) within 1e-5 relative to the
+row's scale.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {
+    "f32": {"abs": 1e-4, "rel": 1e-4, "norm": 1e-5},
+    "bf16": {"abs": 2e-2, "rel": 1e-2, "norm": 1e-2},
+}
+STAT_TOL = 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def to_host64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> float64 numpy, decoding bf16 bits with the oracle's decoder."""
+    if t.dtype == torch.bfloat16:
+        return oracle.decode_bf16(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(pd, eps=None, dense=None):
+    """Forward + backward of one problem on the GPU.  Returns device tensors."""
+    import diffusion_transformer_adaln_amd as adaln
+
+    p = pd.problem
+    eps = p.eps if eps is None else eps
+    dense = p.dense if dense is None else dense
+    x = to_dev(pd.x, p.dtype)
+    dy = to_dev(pd.dy, p.dtype)
+    shift = to_dev(pd.shift, p.dtype)
+    scale = to_dev(pd.scale, p.dtype)
+    if dense:
+        B, N, D = p.B, p.N, p.D
+        y, mean, rstd = adaln.adaln_fwd(x.view(B, N, D), shift, scale, eps)
+        dx, dscale, dshift = adaln.adaln_bwd(dy.view(B, N, D), x.view(B, N, D), scale, mean, rstd)
+        y, dx, mean, rstd = y.view(-1, D), dx.view(-1, D), mean.view(-1), rstd.view(-1)
+    else:
+        off = torch.from_numpy(pd.offsets).cuda()
+        y, mean, rstd = adaln.adaln_fwd_varlen(x, shift, scale, off, eps)
+        dx, dscale, dshift = adaln.adaln_bwd_varlen(dy, x, scale, mean, rstd, off)
+    torch.cuda.synchronize()
+    return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dscale": dscale, "dshift": dshift}
+
+
+def _rows_problem(pd, rows):
+    """Oracle inputs for a set of rows: each row becomes its own one-row sample
+    carrying its original sample's modulation (rows are independent)."""
+    p = pd.problem
+    rows = np.asarray(rows, dtype=np.int64)
+    b = oracle.sample_of_rows(pd.offsets, rows)
+    x = oracle.decode(pd.x[rows], p.dtype)
+    dy = oracle.decode(pd.dy[rows], p.dtype)
+    shift = oracle.decode(pd.shift, p.dtype)[b]
+    scale = oracle.decode(pd.scale, p.dtype)[b]
+    off = np.arange(rows.size + 1, dtype=np.int64)
+    return x, dy, shift, scale, off
+
+
+def assert_abs(got, ref, tol, what):
+    err = np.abs(got - ref)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max abs error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def assert_norm(got, ref, tol, what):
+    if ref.size == 0:
+        return 0.0
+    denom = float(np.abs(ref).max())
+    e = float(np.abs(got - ref).max()) / denom if denom > 0 else float(np.abs(got).max())
+    assert e <= tol, f"{what}: normwise error {e:.3e} > {tol:.1e}"
+    return e
+
+
+def assert_rel_floored(got, ref, tol, what):
+    """Per sample row: |got-ref| / max(|ref|, 1e-3 * rms(ref))."""
+    worst = 0.0
+    for i in range(ref.shape[0]):
+        r = ref[i]
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        if rms == 0.0:
+            e = float(np.abs(got[i]).max()) if r.size else 0.0
+            assert e == 0.0, f"{what}[{i}]: expected exact zeros, max |got| {e:.3e}"
+            continue
+        rel = np.abs(got[i] - r) / np.maximum(np.abs(r), 1e-3 * rms)
+        worst = max(worst, float(rel.max()))
+    assert worst <= tol, f"{what}: max relative error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+def check_rows(pd, out, rows, eps=None):
+    """y, mean, rstd, dx of the given rows against the oracle."""
+    p = pd.problem
+    eps = p.eps if eps is None else eps
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.size == 0:
+        return {}
+    x, dy, shift, scale, off = _rows_problem(pd, rows)
+    y_ref, mean_ref, rstd_ref = oracle.adaln_fwd(x, shift, scale, eps, off)
+    dx_ref, _, _ = oracle.adaln_bwd(dy, x, scale, eps, off)
+    idx = torch.from_numpy(rows).cuda()
+    y = to_host64(out["y"].index_select(0, idx))
+    dx = to_host64(out["dx"].index_select(0, idx))
+    mean = to_host64(out["mean"].index_select(0, idx))
+    rstd = to_host64(out["rstd"].index_select(0, idx))
+    t = TOL[p.dtype]
+    res = {
+        "y_abs": assert_abs(y, y_ref, t["abs"], "y"),
+        "dx_abs": assert_abs(dx, dx_ref, t["abs"], "dx"),
+        "y_norm": assert_norm(y, y_ref, t["norm"], "y"),
+        "dx_norm": assert_norm(dx, dx_ref, t["norm"], "dx"),
+    }
+    row_scale = np.abs(mean_ref) + 1.0 / rstd_ref
+    res["mean"] = assert_abs(np.abs(mean - mean_ref) / row_scale, 0.0, STAT_TOL, "mean")
+    res["rstd"] = assert_abs(np.abs(rstd - rstd_ref) / rstd_ref, 0.0, STAT_TOL, "rstd")
+    return res
+
+
+def check_samples(pd, out, samples, eps=None):
+    """dscale and dshift of the given samples (full column sums) against the oracle."""
+    p = pd.problem
+    eps = p.eps if eps is None else eps
+    samples = np.asarray(samples, dtype=np.int64)
+    if samples.size == 0:
+        return {}
+    ds_ref = np.zeros((samples.size, p.D))
+    dh_ref = np.zeros((samples.size, p.D))
+    scale_all = oracle.decode(pd.scale, p.dtype)
+    for i, b in enumerate(samples):
+        lo, hi = int(pd.offsets[b]), int(pd.offsets[b + 1])
+        if hi == lo:
+            continue
+        x = oracle.decode(pd.x[lo:hi], p.dtype)
+        dy = oracle.decode(pd.dy[lo:hi], p.dtype)
+        _, ds, dh = oracle.adaln_bwd(dy, x, scale_all[b:b + 1], eps, np.array([0, hi - lo]))
+        ds_ref[i], dh_ref[i] = ds[0], dh[0]
+    idx = torch.from_numpy(samples).cuda()
+    ds = to_host64(out["dscale"].index_select(0, idx))
+    dh = to_host64(out["dshift"].index_select(0, idx))
+    t = TOL[p.dtype]
+    return {
+        "dscale_rel": assert_rel_floored(ds, ds_ref, t["rel"], "dscale"),
+        "dshift_rel": assert_rel_floored(dh, dh_ref, t["rel"], "dshift"),
+    }
+
+
+def check_all(pd, out, eps=None):
+    p = pd.problem
+    r = check_rows(pd, out, np.arange(p.R), eps)
+    r.update(check_samples(pd, out, np.arange(p.B), eps))
+    return r
+
+
+def sampled_rows(pd, k=48, seed=0):
+    """Rows for a full-size check: first/last rows of samples and random rows."""
+    p = pd.problem
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = set(g.choice(p.R, size=min(k, p.R), replace=False).tolist())
+    for b in range(0, p.B, max(1, p.B // 8)):
+        lo, hi = int(pd.offsets[b]), int(pd.offsets[b + 1])
+        if hi > lo:
+            rows.update({lo, hi - 1})
+    rows.update({0, p.R - 1})
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def bits(t: torch.Tensor) -> bytes:
+    return t.contiguous().view(torch.uint8).cpu().numpy().tobytes()

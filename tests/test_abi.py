@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every entry point include/adaln.h
+declares, and rejects bad arguments before touching a device (no kernels
+are launched here, and no HIP call is reached on these paths)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import diffusion_transformer_adaln_amd as adaln
+from diffusion_transformer_adaln_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adaln.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(adaln_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        pytest.fail("libadaln.so is not built: run __graft_entry__.build() first")
+    return adaln.load_library()
+
+
+def test_header_matches_binding_and_exports(lib):
+    decl = declared_functions()
+    assert decl == sorted(adaln.EXPORTED), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (adaln_\w+)", out))
+    assert set(decl) <= exported, set(decl) - exported
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.adaln_abi_version() == 1
+    for code, name in adaln._lib.STATUS_NAMES.items():
+        assert adaln.adaln_status_str(code) == name
+    assert adaln.adaln_status_str(99) == "ADALN_ERR_UNKNOWN"
+
+
+P = ctypes.c_void_p
+FAKE = 1 << 20        # distinct fake device addresses: validation never dereferences
+
+
+def fwd(lib, x=FAKE, sh=FAKE * 2, sc=FAKE * 3, eps=1e-6, B=1, N=4, D=8, dt=1, y=FAKE * 4, m=FAKE * 5,
+        r=FAKE * 6):
+    return lib.adaln_fwd(P(x), P(sh), P(sc), eps, B, N, D, dt, None, P(y), P(m), P(r))
+
+
+def bwd(lib, dy=FAKE, x=FAKE * 2, sc=FAKE * 3, m=FAKE * 4, r=FAKE * 5, B=1, N=4, D=8, dt=1, ws=FAKE * 6,
+        wsb=1 << 20, dx=FAKE * 7, ds=FAKE * 8, dh=FAKE * 9):
+    return lib.adaln_bwd(P(dy), P(x), P(sc), P(m), P(r), B, N, D, dt, P(ws), wsb, None, P(dx), P(ds), P(dh))
+
+
+def test_forward_validation_codes(lib):
+    assert fwd(lib, dt=7) == 2                          # unsupported dtype
+    assert fwd(lib, B=0) == 1                           # B < 1
+    assert fwd(lib, N=-1) == 1
+    assert fwd(lib, D=0) == 1
+    assert fwd(lib, D=65537) == 3                       # above ADALN_MAX_D
+    assert fwd(lib, N=1 << 62, D=1024) == 3             # byte count overflows int64
+    assert fwd(lib, eps=float("nan")) == 1
+    assert fwd(lib, eps=float("inf")) == 1
+    assert fwd(lib, eps=-1.0) == 1
+    assert fwd(lib, x=0) == 1                           # null input
+    assert fwd(lib, sh=0) == 1
+    assert fwd(lib, m=0) == 1
+    assert fwd(lib, y=FAKE + 8) == 5                    # y overlaps x
+    assert fwd(lib, m=FAKE * 4 + 16) == 5               # mean overlaps y
+    assert fwd(lib, r=FAKE * 3) == 5                    # rstd overlaps scale
+    assert fwd(lib, N=0, x=0, y=0, m=0, r=0) == 0       # empty batch: nothing to do, no device touched
+
+
+def test_varlen_validation_codes(lib):
+    f = lib.adaln_fwd_varlen
+    assert f(P(FAKE), P(FAKE * 2), P(FAKE * 3), 1e-6, None, 2, 8, 8, 1, None, P(FAKE * 4), P(FAKE * 5),
+             P(FAKE * 6)) == 1                          # null offsets
+    assert f(P(FAKE), P(FAKE * 2), P(FAKE * 3), 1e-6, P(FAKE * 7), 0, 8, 8, 1, None, P(FAKE * 4),
+             P(FAKE * 5), P(FAKE * 6)) == 1             # B < 1
+    assert f(P(FAKE), P(FAKE * 2), P(FAKE * 3), 1e-6, P(FAKE * 7), 2, -1, 8, 1, None, P(FAKE * 4),
+             P(FAKE * 5), P(FAKE * 6)) == 1             # negative rows
+    assert f(P(FAKE), P(FAKE * 2), P(FAKE * 3), 1e-6, P(FAKE * 4 + 8), 2, 8, 8, 1, None, P(FAKE * 4),
+             P(FAKE * 5), P(FAKE * 6)) == 5             # y overlaps offsets
+    b = lib.adaln_bwd_varlen
+    assert b(P(FAKE), P(FAKE * 2), P(FAKE * 3), P(FAKE * 4), P(FAKE * 5), None, 2, 8, 8, 1, P(FAKE * 6),
+             1 << 20, None, P(FAKE * 7), P(FAKE * 8), P(FAKE * 9)) == 1
+
+
+def test_backward_validation_codes(lib):
+    assert bwd(lib, dt=3) == 2
+    assert bwd(lib, B=0) == 1
+    assert bwd(lib, D=70000) == 3
+    assert bwd(lib, dy=0) == 1
+    assert bwd(lib, ds=0) == 1
+    assert bwd(lib, ws=0) == 1                          # no workspace
+    assert bwd(lib, ws=FAKE * 6 + 4) == 1               # workspace not 16-byte aligned
+
+
+def test_workspace_query_rejects_bad_sizes(lib):
+    assert lib.adaln_bwd_workspace_size(0, 10, 8, 1) == 0
+    assert lib.adaln_bwd_workspace_size(1, -1, 8, 1) == 0
+    assert lib.adaln_bwd_workspace_size(1, 10, 0, 1) == 0
+    assert lib.adaln_bwd_workspace_size(1, 10, 8, 5) == 0

@@ -1,0 +1,212 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Small problems (several tiles plus a ragged tail) are checked in full;
+the full-size workloads are checked on sampled rows and on whole-sample
+column sums.  Edge cases: empty inputs and samples, one-row samples, odd and
+tiny D, misaligned pointers (general kernels), the largest supported D,
+constant rows, determinism and dense/packed equivalence.
+"""
+
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import (bits, check_all, check_rows, check_samples, run_gpu, sampled_rows, say,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _pd(dtype, D, lengths, seed=0, dense=None, **kw):
+    p = workloads.custom_problem(dtype, D, lengths, dense=dense, **kw)
+    return workloads.make_problem_data(p, seed)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at sizes the oracle checks in full
+# ---------------------------------------------------------------------------
+SMALL = {
+    "tiny_fp32": lambda: workloads.make_config("tiny_fp32"),
+    "dit_bf16_small": lambda: [_pd("bf16", 1152, [300] * 3, seed=2, dy_sigma=1e-2)],
+    "mmdit_bf16_small": lambda: [
+        _pd("bf16", 3072, [77] * 2, seed=3, dy_sigma=1e-2, outlier_frac=0.01),
+        _pd("bf16", 3072, [513] * 2, seed=4, dy_sigma=1e-2, outlier_frac=0.01)],
+    "video_bf16_small": lambda: [_pd("bf16", 5120, [1000], seed=5, dy_sigma=1e-3)],
+    "ragged_bf16_small": lambda: [_pd("bf16", 3072, [5, 0, 300, 1, 129, 64], seed=6, dense=False)],
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_workloads_full_check(name):
+    for pd in SMALL[name]():
+        say(f"[parity] {name}/{pd.problem.name} R={pd.problem.R} D={pd.problem.D}")
+        out = run_gpu(pd)
+        res = check_all(pd, out)
+        say(f"  {res}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows, whole-sample sums
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["dit_bf16", "mmdit_bf16", "video_bf16", "ragged_bf16"])
+def test_full_size_workloads_sampled(name):
+    for pd in workloads.make_config(name):
+        p = pd.problem
+        say(f"[parity-full] {name}/{p.name} B={p.B} R={p.R} D={p.D}")
+        out = run_gpu(pd)
+        rows = sampled_rows(pd)
+        res = check_rows(pd, out, rows)
+        if p.B <= 8:
+            samples = np.arange(p.B)
+        else:   # one sample of every distinct length, plus the first and last
+            seen, samples = set(), []
+            for b, n in enumerate(p.lengths):
+                if n not in seen:
+                    seen.add(n)
+                    samples.append(b)
+            samples = np.array(sorted(set(samples) | {0, p.B - 1}))
+        res.update(check_samples(pd, out, samples))
+        say(f"  rows={rows.size} samples={len(samples)} {res}")
+        del out
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# shapes: vector plans, general kernels, extremes
+# ---------------------------------------------------------------------------
+SHAPES = [
+    ("f32", 1, [3, 5]), ("f32", 7, [33]), ("f32", 64, [255]), ("f32", 127, [9, 4]),
+    ("f32", 768, [130]), ("f32", 4096, [70]), ("f32", 8192, [17]), ("f32", 12288, [5]),
+    ("bf16", 8, [40]), ("bf16", 64, [255]), ("bf16", 127, [9]), ("bf16", 768, [130, 7]),
+    ("bf16", 1024, [100]), ("bf16", 2048, [64, 64]), ("bf16", 4096, [97]),
+    ("bf16", 8192, [41]), ("bf16", 12288, [9]), ("bf16", 16384, [12]), ("bf16", 20000, [6]),
+    ("bf16", 32768, [4]), ("f32", 65536, [3]), ("bf16", 65536, [3]),
+]
+
+
+@pytest.mark.parametrize("dtype,D,lengths", SHAPES, ids=[f"{d}-D{D}-{'x'.join(map(str, l))}" for d, D, l in SHAPES])
+def test_shapes(dtype, D, lengths):
+    pd = _pd(dtype, D, lengths, seed=D, dy_sigma=1.0 if dtype == "f32" else 1e-2)
+    say(f"[shape] {dtype} D={D} lengths={lengths}")
+    check_all(pd, run_gpu(pd))
+    if len(set(lengths)) > 1 or len(lengths) > 1:
+        check_all(pd, run_gpu(pd, dense=False))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_misaligned_pointers_take_general_path(dtype):
+    import diffusion_transformer_adaln_amd as adaln
+
+    pd = _pd(dtype, 256, [37, 37], seed=9)
+    p = pd.problem
+    say(f"[misaligned] {dtype}")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    n = p.R * p.D
+
+    def shifted(arr):
+        t = to_dev(arr.reshape(-1), dtype)
+        buf = torch.empty(n + 1, dtype=tdt, device="cuda")
+        buf[1:] = t
+        return buf[1:]            # 4- or 2-byte offset from a 256-byte-aligned allocation
+
+    x = shifted(pd.x).view(p.B, p.N, p.D)
+    dy = shifted(pd.dy).view(p.B, p.N, p.D)
+    shift, scale = to_dev(pd.shift, dtype), to_dev(pd.scale, dtype)
+    y, mean, rstd = adaln.adaln_fwd(x, shift, scale, p.eps)
+    dx, ds, dh = adaln.adaln_bwd(dy, x, scale, mean, rstd)
+    out = {"y": y.view(-1, p.D), "mean": mean.view(-1), "rstd": rstd.view(-1), "dx": dx.view(-1, p.D),
+           "dscale": ds, "dshift": dh}
+    check_all(pd, out)
+
+
+def test_empty_batch_and_empty_samples():
+    import diffusion_transformer_adaln_amd as adaln
+
+    say("[empty] N=0 dense")
+    x = torch.empty((2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    shift = torch.randn(2, 64, device="cuda").to(torch.bfloat16)
+    scale = torch.randn(2, 64, device="cuda").to(torch.bfloat16)
+    y, mean, rstd = adaln.adaln_fwd(x, shift, scale, 1e-6)
+    assert y.shape == (2, 0, 64)
+    ds = torch.full((2, 64), 7.0, device="cuda").to(torch.bfloat16)
+    dh = torch.full((2, 64), 7.0, device="cuda").to(torch.bfloat16)
+    adaln.adaln_bwd(x, x.clone(), scale, mean, rstd, dscale=ds, dshift=dh)
+    torch.cuda.synchronize()
+    assert not ds.float().any() and not dh.float().any()
+    say("[empty] varlen with empty samples")
+    pd = _pd("bf16", 3072, [0, 17, 0, 0, 40, 0], seed=11, dense=False)
+    check_all(pd, run_gpu(pd))
+    pd = _pd("f32", 96, [0, 0, 0], seed=12, dense=False)
+    out = run_gpu(pd)
+    assert not out["dscale"].any() and not out["dshift"].any()
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("bf16", 5120), ("bf16", 100)])
+def test_constant_rows(dtype, D):
+    """Zero-variance rows: rstd = eps^-1/2, y = shift, dx = rstd*(g - mean(g))."""
+    pd = _pd(dtype, D, [40], seed=13)
+    const = workloads.encode_bf16_rne(np.full(D, 3.25, np.float32)) if dtype == "bf16" else np.full(D, 3.25, np.float32)
+    pd.x[::3] = const
+    say(f"[constant rows] {dtype} D={D}")
+    for eps in (1e-6, 1e-2):
+        check_all(pd, run_gpu(pd, eps=eps), eps=eps)
+
+
+# ---------------------------------------------------------------------------
+# determinism and dense == packed
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,lengths", [("bf16", 5120, [3000]), ("bf16", 1152, [700] * 4), ("f32", 128, [999])])
+def test_run_to_run_bitwise(dtype, D, lengths):
+    pd = _pd(dtype, D, lengths, seed=21)
+    say(f"[determinism] {dtype} D={D} lengths={lengths}")
+    ref = None
+    for _ in range(10):
+        out = run_gpu(pd)
+        h = {k: hashlib.sha256(bits(v)).hexdigest() for k, v in out.items()}
+        if ref is None:
+            ref = h
+        assert h == ref, "outputs differ between runs"
+
+
+@pytest.mark.parametrize("dtype,D,N,B", [("bf16", 3072, 515, 3), ("f32", 128, 300, 2), ("bf16", 100, 33, 2)])
+def test_dense_equals_packed_bitwise(dtype, D, N, B):
+    pd = _pd(dtype, D, [N] * B, seed=31)
+    say(f"[dense==packed] {dtype} D={D} N={N} B={B}")
+    a = run_gpu(pd, dense=True)
+    b = run_gpu(pd, dense=False)
+    for k in a:
+        assert bits(a[k]) == bits(b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# error codes through the real library
+# ---------------------------------------------------------------------------
+def test_error_codes_on_device():
+    import diffusion_transformer_adaln_amd as adaln
+
+    say("[errors]")
+    x = torch.randn(2, 16, 64, device="cuda").to(torch.bfloat16)
+    sh = torch.zeros(2, 64, device="cuda").to(torch.bfloat16)
+    with pytest.raises(adaln.AdaLNError) as e:
+        adaln.adaln_fwd(x, sh, sh, 1e-6, y=x)                       # output aliases input
+    assert e.value.status == 5
+    y, mean, rstd = adaln.adaln_fwd(x, sh, sh, 1e-6)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(adaln.AdaLNError) as e:
+        adaln.adaln_bwd(x, x, sh, mean, rstd, workspace=small)
+    assert e.value.status == 4
+    with pytest.raises(adaln.AdaLNError) as e:
+        adaln.adaln_fwd(x, sh, sh, float("nan"))
+    assert e.value.status == 1
+    assert adaln.adaln_bwd_workspace_size(2, 32, 64, torch.bfloat16) > 0
+
+
+def test_single_hip_runtime_mapped():
+    import diffusion_transformer_adaln_amd as adaln
+
+    adaln.load_library()
+    libs = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
+    assert len(libs) == 1, libs

@@ -28,6 +28,9 @@ struct Tiling {
   int64_t tile_rows;
   int64_t tiles_max;         // grid size of the row pass (upper bound for varlen)
   int64_t* tile_start;       // device, B+1 entries (varlen only), else nullptr
+  int64_t* group_start;      // device, B+1 entries (varlen only): first finish group of each sample
+  int64_t groups_max;        // finish groups (upper bound for varlen)
+  int interleave;            // 1: tile k of a sample takes rows k, k+tiles, ...; 0: contiguous runs
 };
 
 // Row layout of the vectorised kernels: a row of D elements is V = D/EPV
@@ -63,10 +66,12 @@ size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);
 // Layout of that workspace.
 struct WorkspaceLayout {
   size_t tile_start_off;   // int64 [B+1]
+  size_t group_start_off;  // int64 [B+1]
   size_t partial_off;      // fp32 [tiles_max][2][D]
   size_t total;
   int64_t tile_rows;
   int64_t tiles_max;
+  int64_t groups_max;
 };
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense);

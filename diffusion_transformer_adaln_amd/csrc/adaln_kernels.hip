@@ -94,6 +94,14 @@ template <> struct Elem<BF16> {
   }
 };
 
+// Product rounded to fp32 on its own: never fused into a following add, so a
+// value computed twice (once for a row sum, once for the output) has the
+// same bits both times.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane exchange
 // ---------------------------------------------------------------------------
@@ -184,14 +192,21 @@ __device__ __forceinline__ int64_t sample_of_row(const RowMap& rm, int64_t row) 
   return lo;
 }
 
-__device__ __forceinline__ void tile_bounds(const RowMap& rm, const Tiling& tl, int64_t t,
-                                            int64_t& b, int64_t& r0, int64_t& r1) {
+// Rows of tile t: sample b, rows first + m*step for m in [0, count).
+// Sample b's rows are split over its tiles either in contiguous runs of
+// tile_rows rows (step 1) or, with tl.interleave, round-robin (tile k of the
+// sample takes rows k, k + tiles, k + 2*tiles, ...), which keeps the rows in
+// flight across the chip inside a narrow moving window.
+__device__ __forceinline__ void tile_rows_of(const RowMap& rm, const Tiling& tl, int64_t t,
+                                             int64_t& b, int64_t& first, int64_t& step,
+                                             int64_t& count) {
+  int64_t k, tiles, lo_row, n;
   if (rm.offsets == nullptr) {
-    const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
-    b = t / tps;
-    const int64_t i = t - b * tps;
-    r0 = b * rm.N + i * tl.tile_rows;
-    r1 = b * rm.N + min(rm.N, (i + 1) * tl.tile_rows);
+    tiles = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
+    b = t / tiles;
+    k = t - b * tiles;
+    lo_row = b * rm.N;
+    n = rm.N;
   } else {
     // largest b with tile_start[b] <= t
     int64_t lo = 0, hi = rm.B;
@@ -200,9 +215,19 @@ __device__ __forceinline__ void tile_bounds(const RowMap& rm, const Tiling& tl, 
       if (tl.tile_start[mid] <= t) lo = mid; else hi = mid;
     }
     b = lo;
-    const int64_t i = t - tl.tile_start[b];
-    r0 = rm.offsets[b] + i * tl.tile_rows;
-    r1 = min(rm.offsets[b + 1], r0 + tl.tile_rows);
+    k = t - tl.tile_start[b];
+    tiles = tl.tile_start[b + 1] - tl.tile_start[b];
+    lo_row = rm.offsets[b];
+    n = rm.offsets[b + 1] - lo_row;
+  }
+  if (tl.interleave) {
+    first = lo_row + k;
+    step = tiles;
+    count = (n - k + tiles - 1) / tiles;
+  } else {
+    first = lo_row + k * tl.tile_rows;
+    step = 1;
+    count = min(tl.tile_rows, n - k * tl.tile_rows);
   }
 }
 
@@ -215,16 +240,17 @@ constexpr int VEC_MAX_NT = 512;
 // ---------------------------------------------------------------------------
 // Grid: one workgroup per chunk of `rows_per_wg` consecutive rows.
 // LDS: 2 buffers x [slots][RIF][groups] x (mean, M2).
-// Rows each slot keeps in flight per iteration: about 8 (forward) or 4
-// (backward, two row arrays) 16-byte vectors per lane, which keeps the
-// kernels clear of register spills at two or more waves per SIMD.
-constexpr int fwd_rif(int vpt) { return vpt <= 1 ? 8 : vpt == 2 ? 4 : vpt <= 4 ? 2 : 1; }
-constexpr int bwd_rif(int vpt) { return vpt <= 1 ? 4 : vpt == 2 ? 2 : 1; }
+// Rows each slot handles per loop iteration.  Measured on MI355X, one row
+// per slot with more workgroups resident beats deeper per-slot batching or
+// register prefetch: both cost VGPRs, hence occupancy, which is what keeps
+// HBM requests in flight here.
+constexpr int FWD_RIF = 1;
+constexpr int BWD_RIF = 1;
 constexpr int FWD_MAX_VPT = 8;
 constexpr int BWD_MAX_VPT = 4;
 
-template <int DT, int VPT, int RIF>
-__global__ void __launch_bounds__(VEC_MAX_NT)
+template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT>
+__global__ void __launch_bounds__(NTMAX)
 fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
                const uint4* __restrict__ scale, float eps, RowMap rm, int V, int D, int lpr,
                int64_t rows_per_wg, uint4* __restrict__ y, float* __restrict__ mean,
@@ -250,7 +276,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
   constexpr float n_lane = static_cast<float>(VPT * EPV);
 
   float sc1[VPT][EPV], sh[VPT][EPV];
-  int64_t cur_b = -1;
+  int64_t cur_lo = 0, cur_hi = 0;     // rows of the sample whose modulation is loaded
   int it = 0;
 
   for (int64_t base = r_begin; base < r_end; base += rows_per_iter, ++it) {
@@ -313,9 +339,10 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
       if (!valid[i]) continue;
       const float rs = 1.0f / sqrtf(s[i] * inv_d + eps);
       if (lane == 0) { mean[row[i]] = m[i]; rstd[row[i]] = rs; }
-      const int64_t b = sample_of_row(rm, row[i]);
-      if (b != cur_b) {
-        cur_b = b;
+      if (row[i] >= cur_hi || row[i] < cur_lo) {
+        const int64_t b = sample_of_row(rm, row[i]);
+        cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
+        cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
         const uint4* scp = scale + b * V + lane;
         const uint4* shp = shift + b * V + lane;
 #pragma unroll
@@ -348,8 +375,8 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // Grid: one workgroup per tile (a run of rows inside one sample).
 // LDS: 2 buffers x [slots][RIF][groups] x (sum g, sum g*xhat), then, when a
 // workgroup holds several slots, [2][D] floats for the slot combine.
-template <int DT, int VPT, int RIF>
-__global__ void __launch_bounds__(VEC_MAX_NT)
+template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool PF = true>
+__global__ void __launch_bounds__(NTMAX)
 bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
                const uint4* __restrict__ scale, const float* __restrict__ mean,
                const float* __restrict__ rstd, RowMap rm, Tiling tl, int V, int D, int lpr,
@@ -360,8 +387,8 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 
   const int64_t t = blockIdx.x;
   if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
-  int64_t b, r0, r1;
-  tile_bounds(rm, tl, t, b, r0, r1);
+  int64_t b, first, step, count;
+  tile_rows_of(rm, tl, t, b, first, step, count);
 
   const int tid = threadIdx.x;
   const int nslots = blockDim.x / lpr;
@@ -390,24 +417,37 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
     for (int k = 0; k < EPV; ++k) { acc_h[j][k] = 0.f; acc_s[j][k] = 0.f; }
 
-  const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
-  int it = 0;
-  for (int64_t base = r0; base < r1; base += rows_per_iter, ++it) {
-    uint4 xv[RIF][VPT], gv[RIF][VPT];
-    int64_t row[RIF];
-    bool valid[RIF];
-    float mu[RIF], rs[RIF];
+  // One iteration's rows: this slot takes tile rows m = base + slot*RIF + i.
+  // Rows past the tile's end load the tile's first row instead (always
+  // valid) and are then ignored.
+  uint4 xv[RIF][VPT], gv[RIF][VPT];
+  float mu[RIF], rs[RIF];
+  auto load_rows = [&](int64_t base, uint4 (&xa)[RIF][VPT], uint4 (&ga)[RIF][VPT], float (&ma)[RIF],
+                       float (&ra)[RIF]) {
 #pragma unroll
     for (int i = 0; i < RIF; ++i) {
-      row[i] = base + static_cast<int64_t>(slot) * RIF + i;
-      valid[i] = row[i] < r1;
-      const int64_t rr = valid[i] ? row[i] : r0;
-      mu[i] = mean[rr];
-      rs[i] = rstd[rr];
+      const int64_t m = base + static_cast<int64_t>(slot) * RIF + i;
+      const int64_t rr = m < count ? first + m * step : first;
+      ma[i] = mean[rr];
+      ra[i] = rstd[rr];
       const uint4* xr = x + rr * V + lane;
       const uint4* gr = dy + rr * V + lane;
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) { xv[i][j] = xr[j * lpr]; gv[i][j] = gr[j * lpr]; }
+      for (int j = 0; j < VPT; ++j) { xa[i][j] = xr[j * lpr]; ga[i][j] = gr[j * lpr]; }
+    }
+  };
+
+  const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
+  int it = 0;
+  if (PF) load_rows(0, xv, gv, mu, rs);
+  for (int64_t base = 0; base < count; base += rows_per_iter, ++it) {
+    // with PF the next iteration's loads are in flight while this one reduces
+    uint4 xn[RIF][VPT], gn[RIF][VPT];
+    float mun[RIF], rsn[RIF];
+    if (PF) {
+      if (base + rows_per_iter < count) load_rows(base + rows_per_iter, xn, gn, mun, rsn);
+    } else {
+      load_rows(base, xv, gv, mu, rs);
     }
 
     float sg[RIF], sgx[RIF];
@@ -422,7 +462,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           const float xh = (fx[k] - mu[i]) * rs[i];
-          const float g = fg[k] * sc1[j][k];
+          const float g = mul_rounded(fg[k], sc1[j][k]);   // same rounding in both passes
           a += g;
           c += g * xh;
         }
@@ -449,9 +489,11 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 
 #pragma unroll
     for (int i = 0; i < RIF; ++i) {
-      if (!valid[i]) continue;
+      const int64_t m = base + static_cast<int64_t>(slot) * RIF + i;
+      if (m >= count) continue;
+      const int64_t row = first + m * step;
       const float a = sg[i] * inv_d, c = sgx[i] * inv_d;
-      uint4* dxr = dx + row[i] * V + lane;
+      uint4* dxr = dx + row * V + lane;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         float fx[EPV], fg[EPV], out[EPV];
@@ -460,12 +502,20 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           const float xh = (fx[k] - mu[i]) * rs[i];
-          const float g = fg[k] * sc1[j][k];
+          const float g = mul_rounded(fg[k], sc1[j][k]);   // same rounding in both passes
           out[k] = rs[i] * ((g - a) - xh * c);
           acc_h[j][k] += fg[k];
           acc_s[j][k] += fg[k] * xh;
         }
         dxr[j * lpr] = E::pack(out);
+      }
+    }
+    if (PF) {
+#pragma unroll
+      for (int i = 0; i < RIF; ++i) {
+        mu[i] = mun[i]; rs[i] = rsn[i];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) { xv[i][j] = xn[i][j]; gv[i][j] = gn[i][j]; }
       }
     }
   }
@@ -564,20 +614,21 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
   __shared__ float red[4][GEN_NT / 64];
   const int64_t t = blockIdx.x;
   if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;
-  int64_t b, r0, r1;
-  tile_bounds(rm, tl, t, b, r0, r1);
+  int64_t b, first, step, count;
+  tile_rows_of(rm, tl, t, b, first, step, count);
   float* ph = partial + t * 2 * static_cast<int64_t>(D);
   float* ps = ph + D;
   for (int d = threadIdx.x; d < D; d += GEN_NT) { ph[d] = 0.f; ps[d] = 0.f; }
   const float inv_d = 1.0f / static_cast<float>(D);
   int k = 0;
-  for (int64_t r = r0; r < r1; ++r) {
+  for (int64_t m = 0; m < count; ++m) {
+    const int64_t r = first + m * step;
     const int64_t base = r * D;
     const float mu = mean[r], rs = rstd[r];
     float a = 0.f, c = 0.f;
     for (int d = threadIdx.x; d < D; d += GEN_NT) {
       const float xh = (E::load1(x, base + d) - mu) * rs;
-      const float g = E::load1(dy, base + d) * (1.0f + E::load1(scale, b * D + d));
+      const float g = mul_rounded(E::load1(dy, base + d), 1.0f + E::load1(scale, b * D + d));
       a += g; c += g * xh;
     }
     a = block_sum(a, red[(k++) & 3]) * inv_d;
@@ -585,7 +636,7 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
     for (int d = threadIdx.x; d < D; d += GEN_NT) {
       const float xh = (E::load1(x, base + d) - mu) * rs;
       const float gy = E::load1(dy, base + d);
-      const float g = gy * (1.0f + E::load1(scale, b * D + d));
+      const float g = mul_rounded(gy, 1.0f + E::load1(scale, b * D + d));
       E::store1(dx, base + d, rs * ((g - a) - xh * c));
       ph[d] += gy;
       ps[d] += gy * xh;
@@ -596,141 +647,235 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // ---------------------------------------------------------------------------
 // finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
 // ---------------------------------------------------------------------------
-// Workgroup = FIN_COLS column lanes x FIN_SLICES tile slices.  Slice k adds
-// tiles k, k+FIN_SLICES, ... in ascending order; the slices are then added in
-// ascending slice order through LDS.  The grouping depends only on the tile
-// count, so the result is the same on every run.
+// Two short kernels, both with a fixed summation order (so the result is the
+// same on every run):
+//   stage 1  sample b's tiles are cut into groups of FIN_GROUP consecutive
+//            tiles; one workgroup per (group, 64-column chunk) adds the group's
+//            tiles in fp64 (slice k takes tiles k, k+SLICES, ... in ascending
+//            order; slices are then added in ascending order) and writes the
+//            fp32 result over the group's first tile.  One-tile groups are
+//            already summed and exit at once.
+//   stage 2  one workgroup per (sample, 64-column chunk) adds the sample's
+//            group sums in ascending group order in fp64 and stores dscale and
+//            dshift once, rounded to the output type.
+// Spreading stage 1 over (groups x chunks) workgroups keeps every load of the
+// partial sums in flight at once instead of walking hundreds of tiles serially.
 constexpr int FIN_COLS = 64;
+constexpr int FIN_GROUP = 32;
 constexpr int FIN_SLICES = 4;
 
-template <int DT>
-__global__ void __launch_bounds__(FIN_COLS * FIN_SLICES)
-finish_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks,
-              void* __restrict__ dscale, void* __restrict__ dshift) {
-  using E = Elem<DT>;
-  __shared__ float sh_h[FIN_SLICES][FIN_COLS];
-  __shared__ float sh_s[FIN_SLICES][FIN_COLS];
-  const int64_t b = blockIdx.x / col_blocks;
-  const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
-  const int lane = threadIdx.x % FIN_COLS;
-  const int slice = threadIdx.x / FIN_COLS;
-  const int d = cb * FIN_COLS + lane;
-
-  int64_t t0, t1;
+// Tiles [t0, t1) of sample b, and for stage 1 the range of group gi.
+__device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl, int64_t b,
+                                             int64_t& t0, int64_t& t1) {
   if (rm.offsets == nullptr) {
     const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
     t0 = b * tps; t1 = t0 + tps;
   } else {
     t0 = tl.tile_start[b]; t1 = tl.tile_start[b + 1];
   }
-  float h = 0.f, s = 0.f;
-  if (d < D) {
-    const int64_t stride = 2 * static_cast<int64_t>(D);
-    for (int64_t t = t0 + slice; t < t1; t += FIN_SLICES) {
-      h += partial[t * stride + d];
-      s += partial[t * stride + D + d];
+}
+
+__device__ __forceinline__ bool group_tiles(const RowMap& rm, const Tiling& tl, int64_t gi,
+                                            int64_t& t0, int64_t& t1) {
+  int64_t b, k;
+  if (rm.offsets == nullptr) {
+    const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
+    const int64_t gps = (tps + FIN_GROUP - 1) / FIN_GROUP;
+    if (gps == 0) return false;
+    b = gi / gps; k = gi - b * gps;
+    if (b >= rm.B) return false;
+  } else {
+    if (gi >= tl.group_start[rm.B]) return false;
+    int64_t lo = 0, hi = rm.B;     // largest b with group_start[b] <= gi
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (tl.group_start[mid] <= gi) lo = mid; else hi = mid;
     }
+    b = lo; k = gi - tl.group_start[b];
+  }
+  int64_t s0, s1;
+  sample_tiles(rm, tl, b, s0, s1);
+  t0 = s0 + k * FIN_GROUP;
+  t1 = min(s1, t0 + FIN_GROUP);
+  return t1 - t0 > 1;
+}
+
+template <int SLICES>
+__global__ void __launch_bounds__(FIN_COLS * SLICES)
+finish_groups_kernel(float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks) {
+  __shared__ double sh_h[SLICES][FIN_COLS];
+  __shared__ double sh_s[SLICES][FIN_COLS];
+  const int64_t gi = blockIdx.x / col_blocks;
+  const int cb = blockIdx.x - static_cast<int>(gi * col_blocks);
+  int64_t t0, t1;
+  if (!group_tiles(rm, tl, gi, t0, t1)) return;      // whole workgroup: uniform
+  const int lane = threadIdx.x % FIN_COLS;
+  const int slice = threadIdx.x / FIN_COLS;
+  const int d = cb * FIN_COLS + lane;
+  const int64_t stride = 2 * static_cast<int64_t>(D);
+  double h = 0.0, s = 0.0;
+  if (d < D) {
+    constexpr int PER = (FIN_GROUP + SLICES - 1) / SLICES;
+    float vh[PER], vs[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int64_t t = t0 + slice + u * SLICES;
+      vh[u] = t < t1 ? partial[t * stride + d] : 0.f;
+      vs[u] = t < t1 ? partial[t * stride + D + d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
   }
   sh_h[slice][lane] = h;
   sh_s[slice][lane] = s;
   __syncthreads();
   if (slice == 0 && d < D) {
-    float hh = sh_h[0][lane], ss = sh_s[0][lane];
+    double hh = sh_h[0][lane], ss = sh_s[0][lane];
 #pragma unroll
-    for (int k = 1; k < FIN_SLICES; ++k) { hh += sh_h[k][lane]; ss += sh_s[k][lane]; }
-    E::store1(dshift, b * D + d, hh);
-    E::store1(dscale, b * D + d, ss);
+    for (int k = 1; k < SLICES; ++k) { hh += sh_h[k][lane]; ss += sh_s[k][lane]; }
+    partial[t0 * stride + d] = static_cast<float>(hh);
+    partial[t0 * stride + D + d] = static_cast<float>(ss);
   }
 }
 
+template <int DT>
+__global__ void __launch_bounds__(FIN_COLS)
+finish_samples_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D,
+                      int col_blocks, void* __restrict__ dscale, void* __restrict__ dshift) {
+  using E = Elem<DT>;
+  const int64_t b = blockIdx.x / col_blocks;
+  const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
+  const int d = cb * FIN_COLS + threadIdx.x;
+  if (d >= D) return;
+  int64_t t0, t1;
+  sample_tiles(rm, tl, b, t0, t1);
+  const int64_t stride = 2 * static_cast<int64_t>(D);
+  double h = 0.0, s = 0.0;
+  int64_t t = t0;
+  for (; t + 7 * FIN_GROUP < t1; t += 8 * FIN_GROUP) {
+    float vh[8], vs[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      vh[u] = partial[(t + u * FIN_GROUP) * stride + d];
+      vs[u] = partial[(t + u * FIN_GROUP) * stride + D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
+  }
+  for (; t < t1; t += FIN_GROUP) {
+    h += static_cast<double>(partial[t * stride + d]);
+    s += static_cast<double>(partial[t * stride + D + d]);
+  }
+  E::store1(dshift, b * D + d, static_cast<float>(h));
+  E::store1(dscale, b * D + d, static_cast<float>(s));
+}
+
 // ---------------------------------------------------------------------------
-// varlen prologue: tile_start[b] = sum_{c<b} ceil(rows_c / tile_rows)
+// varlen prologue: tile_start[b]  = sum_{c<b} ceil(rows_c / tile_rows)
+//                  group_start[b] = sum_{c<b} ceil(tiles_c / FIN_GROUP)
 // ---------------------------------------------------------------------------
 constexpr int PRO_NT = 1024;
 
 __global__ void __launch_bounds__(PRO_NT)
 varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile_rows,
-                    int64_t* __restrict__ tile_start) {
-  __shared__ int64_t scan[PRO_NT];
-  __shared__ int64_t carry;
-  if (threadIdx.x == 0) carry = 0;
+                    int64_t* __restrict__ tile_start, int64_t* __restrict__ group_start) {
+  __shared__ int64_t scan_t[PRO_NT];
+  __shared__ int64_t scan_g[PRO_NT];
+  __shared__ int64_t carry_t, carry_g;
+  if (threadIdx.x == 0) { carry_t = 0; carry_g = 0; }
   __syncthreads();
   for (int64_t base = 0; base < B; base += PRO_NT) {
     const int64_t b = base + threadIdx.x;
-    int64_t cnt = 0;
+    int64_t ct = 0, cg = 0;
     if (b < B) {
       const int64_t n = offsets[b + 1] - offsets[b];
-      cnt = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
+      ct = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
+      cg = (ct + FIN_GROUP - 1) / FIN_GROUP;
     }
-    scan[threadIdx.x] = cnt;
+    scan_t[threadIdx.x] = ct;
+    scan_g[threadIdx.x] = cg;
     __syncthreads();
-    // Hillis-Steele inclusive scan over the chunk
+    // Hillis-Steele inclusive scans over the chunk
     for (int off = 1; off < PRO_NT; off <<= 1) {
-      const int64_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+      const int64_t vt = threadIdx.x >= off ? scan_t[threadIdx.x - off] : 0;
+      const int64_t vg = threadIdx.x >= off ? scan_g[threadIdx.x - off] : 0;
       __syncthreads();
-      scan[threadIdx.x] += v;
+      scan_t[threadIdx.x] += vt;
+      scan_g[threadIdx.x] += vg;
       __syncthreads();
     }
-    if (b < B) tile_start[b] = carry + scan[threadIdx.x] - cnt;   // exclusive
+    if (b < B) {
+      tile_start[b] = carry_t + scan_t[threadIdx.x] - ct;   // exclusive
+      group_start[b] = carry_g + scan_g[threadIdx.x] - cg;
+    }
     __syncthreads();
-    if (threadIdx.x == PRO_NT - 1) carry += scan[PRO_NT - 1];
+    if (threadIdx.x == PRO_NT - 1) { carry_t += scan_t[PRO_NT - 1]; carry_g += scan_g[PRO_NT - 1]; }
     __syncthreads();
   }
-  if (threadIdx.x == 0) tile_start[B] = carry;
+  if (threadIdx.x == 0) { tile_start[B] = carry_t; group_start[B] = carry_g; }
 }
 
 // ---------------------------------------------------------------------------
 // plans and launchers
 // ---------------------------------------------------------------------------
-// Vector counts per lane tried in order; the first that gives a lane count
-// that is a multiple of 16 (and at most 1024) wins, preferring whole waves.
-static const int kVptOrderBf16[] = {2, 3, 4, 1, 5, 6, 8, 7};
-static const int kVptOrderF32[] = {2, 4, 3, 1, 5, 6, 8, 7};
-
 // Dynamic LDS of a vectorised launch: double-buffered per-row reduction
 // partials, plus the [2][D] slot-combine buffer of a multi-slot backward.
 static size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
   const int nslots = p.nt / p.lpr;
   const int unit = (p.lpr % 64 == 0) ? 64 : (p.lpr == 32 ? 32 : 16);
   const int groups = p.lpr / unit;
-  const int rif = backward ? bwd_rif(p.vpt) : fwd_rif(p.vpt);
+  const int rif = backward ? BWD_RIF : FWD_RIF;
   size_t b = groups > 1 || backward ? 2 * static_cast<size_t>(nslots) * rif * groups * sizeof(float2) : 0;
   if (backward && nslots > 1) b += 2 * static_cast<size_t>(D) * sizeof(float);
   return b;
 }
 
+// Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,
+// LPR a multiple of 16.  Measured on MI355X (video shape, D = 5120 bf16):
+//   forward  about 40 elements per lane (two waves per row at D = 5120) with
+//            two rows per workgroup is fastest; one wave per row runs out of
+//            registers, and wide rows of 8-16 elements per lane spend their
+//            time in cross-wave reductions;
+//   backward 16 elements per lane (VPT = 2) keeps the per-column
+//            accumulators, the modulation row and the row data small enough
+//            for four waves per SIMD.
+// Ties prefer rows that cover whole waves (no partial-wave reductions).
 VecPlan plan_vec(int dtype, int64_t D, bool backward) {
-  VecPlan p{false, 0, 0, 0};
+  VecPlan best{false, 0, 0, 0};
   const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
   const int epv = dtype == BF16 ? 8 : 4;
-  if (D <= 0 || D % epv != 0) return p;
+  if (D <= 0 || D % epv != 0) return best;
   const int64_t V = D / epv;
-  const int* order = dtype == BF16 ? kVptOrderBf16 : kVptOrderF32;
-  for (int pass = 0; pass < 2 && !p.ok; ++pass) {
-    for (int i = 0; i < 8; ++i) {
-      const int vpt = order[i];
-      if (vpt > max_vpt || V % vpt) continue;
-      const int64_t lpr = V / vpt;
-      if (lpr % 16 || lpr > VEC_MAX_NT) continue;
-      if (pass == 0 && lpr % 64) continue;     // first pass: whole waves only
-      p.ok = true; p.vpt = vpt; p.lpr = static_cast<int>(lpr);
-      break;
-    }
+  const int want = backward ? 16 : 40;           // elements per lane
+  int best_score = 1 << 30;
+  for (int vpt = 1; vpt <= max_vpt; ++vpt) {
+    if (V % vpt) continue;
+    const int64_t lpr = V / vpt;
+    if (lpr % 16 || lpr > VEC_MAX_NT) continue;
+    VecPlan p{true, vpt, static_cast<int>(lpr), 0};
+    // threads per workgroup: a multiple of both the row lanes and the wave;
+    // forward rows shorter than 256 lanes are paired up in one workgroup,
+    // backward rows get a workgroup of their own unless they are short
+    int nt = p.lpr;
+    while (nt % 64) nt += p.lpr;
+    const int min_nt = backward ? 128 : 256;
+    while (nt < min_nt && nt * 2 <= VEC_MAX_NT) nt *= 2;
+    if (nt > VEC_MAX_NT) continue;
+    p.nt = nt;
+    if (vec_lds_bytes(p, D, backward) > 65536) continue;
+    const int el = vpt * epv;
+    const int score = (el > want ? el - want : want - el) + (lpr % 64 ? 16 : 0);
+    if (score < best_score) { best_score = score; best = p; }
   }
-  if (!p.ok) return p;
-  // threads per workgroup: a multiple of both the row lanes and the wave,
-  // grown to at least 256 threads when the rows are short
-  int nt = p.lpr;
-  while (nt % 64) nt += p.lpr;
-  while (nt < 256 && nt * 2 <= VEC_MAX_NT) nt *= 2;
-  if (nt > VEC_MAX_NT) { p.ok = false; return p; }
-  p.nt = nt;
-  if (vec_lds_bytes(p, D, backward) > 65536) p.ok = false;
-  return p;
+  return best;
 }
 
+// Backward tiles per compute unit (a tile's column partials cost 8*D bytes
+// written and read again, so fewer, longer tiles are cheaper; two per CU
+// measured best), and the forward's workgroup count per CU (many short-lived
+// workgroups keep the rows in flight inside a narrow window of memory).
 constexpr int BWD_TILES_PER_CU = 2;
-constexpr int FWD_WG_PER_CU = 4;
+constexpr int FWD_WG_PER_CU = 32;
 
 int64_t bwd_tile_rows(int64_t R, int num_cu) {
   const int64_t target = static_cast<int64_t>(num_cu) * BWD_TILES_PER_CU;
@@ -744,10 +889,17 @@ WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu
   WorkspaceLayout w{};
   w.tile_rows = bwd_tile_rows(R, num_cu);
   const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;
-  if (varlen) w.tiles_max = bound;
-  else w.tiles_max = B * ((N_dense + w.tile_rows - 1) / w.tile_rows);
+  if (varlen) {
+    w.tiles_max = bound;
+    w.groups_max = (bound + FIN_GROUP - 1) / FIN_GROUP + B;
+  } else {
+    const int64_t tps = (N_dense + w.tile_rows - 1) / w.tile_rows;
+    w.tiles_max = B * tps;
+    w.groups_max = B * ((tps + FIN_GROUP - 1) / FIN_GROUP);
+  }
   w.tile_start_off = 0;
-  w.partial_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
+  w.group_start_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
+  w.partial_off = w.group_start_off + align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
   w.total = w.partial_off + static_cast<size_t>(bound) * 2 * static_cast<size_t>(D) * sizeof(float);
   return w;
 }
@@ -761,7 +913,7 @@ static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* s
                                  const RowMap& rm, int64_t D, const VecPlan& vp, int num_cu,
                                  hipStream_t stream, void* y, float* mean, float* rstd) {
   constexpr int EPV = Elem<DT>::EPV;
-  constexpr int RIF = fwd_rif(VPT);
+  constexpr int RIF = FWD_RIF;
   const int V = static_cast<int>(D / EPV);
   const int nslots = vp.nt / vp.lpr;
   const size_t lds = vec_lds_bytes(vp, D, false);
@@ -783,10 +935,10 @@ static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scal
                                  int64_t D, const VecPlan& vp, const Tiling& tl, float* partial,
                                  hipStream_t stream, void* dx) {
   constexpr int EPV = Elem<DT>::EPV;
-  constexpr int RIF = bwd_rif(VPT);
+  constexpr int RIF = BWD_RIF;
   const int V = static_cast<int>(D / EPV);
   const size_t lds = vec_lds_bytes(vp, D, true);
-  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF>), dim3(static_cast<unsigned>(tl.tiles_max)),
+  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF, VEC_MAX_NT, false>), dim3(static_cast<unsigned>(tl.tiles_max)),
                      dim3(vp.nt), lds, stream, static_cast<const uint4*>(dy),
                      static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
                      tl, V, static_cast<int>(D), vp.lpr, partial, static_cast<uint4*>(dx));
@@ -827,7 +979,7 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
   hipError_t e = hipSuccess;
   if (rm.offsets != nullptr) {
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       tl.tile_rows, tl.tile_start);
+                       tl.tile_rows, tl.tile_start, tl.group_start);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rm.R > 0 && tl.tiles_max > 0) {
@@ -848,10 +1000,16 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
     if (e != hipSuccess) return e;
   }
   const int col_blocks = static_cast<int>((D + FIN_COLS - 1) / FIN_COLS);
-  const int64_t grid = rm.B * col_blocks;
-  hipLaunchKernelGGL((finish_kernel<DT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(FIN_COLS * FIN_SLICES), 0, stream, partial, rm, tl, static_cast<int>(D),
-                     col_blocks, dscale, dshift);
+  if (rm.R > 0 && tl.groups_max > 0) {
+    hipLaunchKernelGGL((finish_groups_kernel<FIN_SLICES>),
+                       dim3(static_cast<unsigned>(tl.groups_max * col_blocks)),
+                       dim3(FIN_COLS * FIN_SLICES), 0, stream, partial, rm, tl, static_cast<int>(D),
+                       col_blocks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((finish_samples_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),
+                     dim3(FIN_COLS), 0, stream, partial, rm, tl, static_cast<int>(D), col_blocks,
+                     dscale, dshift);
   return hipGetLastError();
 }
 

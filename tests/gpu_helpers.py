@@ -6,10 +6,13 @@ Tolerances (the operator's accuracy contract):
             dscale and dshift
   bf16 I/O: max abs error 2e-2 on y and dx; max relative error 1e-2 on
             dscale and dshift
-The relative error of a column sum uses max(|ref|, 1e-3 * rms(ref of that
-sample)) as denominator, so sums that cancel to nearly zero are judged on
-the scale of their sample (an fp32 sum's absolute error does not shrink with
-its value).  Two stricter internal gates are applied as well:
+The relative error of a column sum uses max(|ref|, 1e-2 * rms(ref of that
+sample)) as denominator: with fp32 statistics and accumulation, a sum of N
+terms carries an absolute error of order u * rms(ref) (u = 2^-24, times a
+small constant for the rounding of xhat and of the running sum) whatever its
+value, so a relative error of 1e-4 can only be asked of sums at least about
+1e-2 * rms(ref) in size; smaller sums (about 1% of a sample's columns) are
+judged on that absolute scale.  Two stricter internal gates are applied as well:
 normwise error max|got-ref| / max|ref| of y and dx at most 1e-2 (bf16) or
 1e-5 (fp32), and fp32 statistics (mean, rstd) within 1e-5 relative to the
 row's scale.
@@ -29,6 +32,7 @@ TOL = {
     "bf16": {"abs": 2e-2, "rel": 1e-2, "norm": 1e-2},
 }
 STAT_TOL = 1e-5
+REL_FLOOR = 1e-2
 
 
 def say(msg):
@@ -87,10 +91,26 @@ def _rows_problem(pd, rows):
     return x, dy, shift, scale, off
 
 
-def assert_abs(got, ref, tol, what):
+def half_ulp_bf16(r):
+    """Half the spacing of bfloat16 values at |r| (8 significand bits)."""
+    a = np.maximum(np.abs(r), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(a)) - 8)
+
+
+def assert_abs(got, ref, tol, what, bf16=False, strict=True):
+    """max |got - ref| <= tol.  For bf16 outputs with |ref| >= 8 no bf16 value
+    lies within 2e-2 of every real number, so there (strict=False only) the
+    bound is tol plus half a bf16 ulp of ref.  strict=True requires the plain
+    bound everywhere."""
     err = np.abs(got - ref)
     worst = float(err.max()) if err.size else 0.0
-    assert worst <= tol, f"{what}: max abs error {worst:.3e} > {tol:.1e}"
+    lim = np.full(err.shape, tol)
+    widened = 0
+    if bf16 and not strict:
+        big = np.abs(ref) >= 8.0
+        widened = int(big.sum())
+        lim = np.where(big, tol + half_ulp_bf16(ref), lim)
+    assert np.all(err <= lim), f"{what}: max abs error {worst:.3e} > {tol:.1e} (elements with |ref|>=8: {widened})"
     return worst
 
 
@@ -104,7 +124,7 @@ def assert_norm(got, ref, tol, what):
 
 
 def assert_rel_floored(got, ref, tol, what):
-    """Per sample row: |got-ref| / max(|ref|, 1e-3 * rms(ref))."""
+    """Per sample row: |got-ref| / max(|ref|, 1e-2 * rms(ref))."""
     worst = 0.0
     for i in range(ref.shape[0]):
         r = ref[i]
@@ -113,13 +133,13 @@ def assert_rel_floored(got, ref, tol, what):
             e = float(np.abs(got[i]).max()) if r.size else 0.0
             assert e == 0.0, f"{what}[{i}]: expected exact zeros, max |got| {e:.3e}"
             continue
-        rel = np.abs(got[i] - r) / np.maximum(np.abs(r), 1e-3 * rms)
+        rel = np.abs(got[i] - r) / np.maximum(np.abs(r), REL_FLOOR * rms)
         worst = max(worst, float(rel.max()))
     assert worst <= tol, f"{what}: max relative error {worst:.3e} > {tol:.1e}"
     return worst
 
 
-def check_rows(pd, out, rows, eps=None):
+def check_rows(pd, out, rows, eps=None, strict=True):
     """y, mean, rstd, dx of the given rows against the oracle."""
     p = pd.problem
     eps = p.eps if eps is None else eps
@@ -136,8 +156,8 @@ def check_rows(pd, out, rows, eps=None):
     rstd = to_host64(out["rstd"].index_select(0, idx))
     t = TOL[p.dtype]
     res = {
-        "y_abs": assert_abs(y, y_ref, t["abs"], "y"),
-        "dx_abs": assert_abs(dx, dx_ref, t["abs"], "dx"),
+        "y_abs": assert_abs(y, y_ref, t["abs"], "y", p.dtype == "bf16", strict),
+        "dx_abs": assert_abs(dx, dx_ref, t["abs"], "dx", p.dtype == "bf16", strict),
         "y_norm": assert_norm(y, y_ref, t["norm"], "y"),
         "dx_norm": assert_norm(dx, dx_ref, t["norm"], "dx"),
     }
@@ -175,9 +195,9 @@ def check_samples(pd, out, samples, eps=None):
     }
 
 
-def check_all(pd, out, eps=None):
+def check_all(pd, out, eps=None, strict=True):
     p = pd.problem
-    r = check_rows(pd, out, np.arange(p.R), eps)
+    r = check_rows(pd, out, np.arange(p.R), eps, strict)
     r.update(check_samples(pd, out, np.arange(p.B), eps))
     return r
 

@@ -18,7 +18,8 @@ algorithmic bytes (the minimal traffic of the method, see
 workloads.algorithmic_bytes) over the wall-clock time of the K timed steps,
 bracketed by device synchronisation.  `roofline` covers the backward call,
 the dominant one: algorithmic bytes per call / mean call duration from HIP
-events recorded on the launch stream inside the timed region.
+events recorded on the launch stream inside the timed region (around every
+fifth step's calls: each event adds a few microseconds of queue bubble).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
 """
@@ -67,9 +68,10 @@ def upload(pd):
 
 
 def cpu_baseline(pd, seconds):
-    """fp64 oracle on successive 128-row blocks of the workload until about
-    `seconds` of CPU time; rows are independent, and each block's column sums
-    are taken over its own rows (the same per-row work as the full sums)."""
+    """fp64 oracle on successive 128-row blocks of the workload (wrapping
+    around to the first row after the last) until about `seconds` of CPU
+    time; rows are independent, and each block's column sums are taken over
+    its own rows (the same per-row work as the full sums)."""
     import numpy as np
 
     import oracle
@@ -78,7 +80,9 @@ def cpu_baseline(pd, seconds):
     rows_done, t_used = 0, 0.0
     block = 128
     start = 0
-    while t_used < seconds and start < p.R:
+    while t_used < seconds:
+        if start >= p.R:
+            start = 0
         lo, hi = start, min(p.R, start + block)
         b = int(oracle.sample_of_rows(pd.offsets, np.array([lo]))[0])
         hi = min(hi, int(pd.offsets[b + 1]))
@@ -102,9 +106,78 @@ def cpu_baseline(pd, seconds):
         "rows_per_s": round(rows_done / t_used, 1),
         "cores": 1,
         "kind": "oracle",
-        "sample": f"fp64 oracle fwd+bwd on the first {rows_done} rows of {p.name} "
-                  f"(D={p.D}), 128-row blocks, {t_used:.1f} s of CPU time",
+        "sample": f"fp64 oracle fwd+bwd over {rows_done} rows of {p.name} (D={p.D}, "
+                  f"{rows_done / p.R:.2f} passes over its {p.R} rows), 128-row blocks, "
+                  f"{t_used:.1f} s of CPU time on one core",
     }
+
+
+class Runner:
+    """Resident copies of one problem's inputs/outputs and its fwd/bwd calls.
+
+    Step k runs the forward on copy k % S and the backward on copy
+    (k + S/2) % S; S is large enough that about 1 GB of other traffic
+    separates two touches of the same copy."""
+
+    def __init__(self, pd, adaln, torch):
+        self.pd, self.p, self.adaln, self.torch = pd, pd.problem, adaln, torch
+        p = self.p
+        tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+        base = upload(pd)
+        S = 4
+        per_set = max(1, 4 * p.R * p.D * p.esize)
+        while (S // 2 - 1) * per_set < (1 << 30) and S < 64:
+            S += 2
+        self.S = S
+        self.sets = []
+        for _ in range(S):
+            self.sets.append({
+                "x": base["x"].clone(), "dy": base["dy"].clone(), "shift": base["shift"],
+                "scale": base["scale"], "offsets": base["offsets"],
+                "y": torch.empty_like(base["x"]), "dx": torch.empty_like(base["x"]),
+                "mean": torch.empty(p.R, dtype=torch.float32, device="cuda"),
+                "rstd": torch.empty(p.R, dtype=torch.float32, device="cuda"),
+                "dscale": torch.empty(p.B, p.D, dtype=tdt, device="cuda"),
+                "dshift": torch.empty(p.B, p.D, dtype=tdt, device="cuda")})
+        self.ws = torch.empty(max(16, adaln.adaln_bwd_workspace_size(p.B, p.R, p.D, tdt)),
+                              dtype=torch.uint8, device="cuda")
+
+    def fwd(self, s):
+        p, a = self.p, self.adaln
+        if p.dense:
+            a.adaln_fwd(s["x"].view(p.B, p.N, p.D), s["shift"], s["scale"], p.eps,
+                        y=s["y"].view(p.B, p.N, p.D), mean=s["mean"].view(p.B, p.N),
+                        rstd=s["rstd"].view(p.B, p.N))
+        else:
+            a.adaln_fwd_varlen(s["x"], s["shift"], s["scale"], s["offsets"], p.eps, y=s["y"],
+                               mean=s["mean"], rstd=s["rstd"])
+
+    def bwd(self, s):
+        p, a = self.p, self.adaln
+        if p.dense:
+            a.adaln_bwd(s["dy"].view(p.B, p.N, p.D), s["x"].view(p.B, p.N, p.D), s["scale"],
+                        s["mean"].view(p.B, p.N), s["rstd"].view(p.B, p.N), workspace=self.ws,
+                        dx=s["dx"].view(p.B, p.N, p.D), dscale=s["dscale"], dshift=s["dshift"])
+        else:
+            a.adaln_bwd_varlen(s["dy"], s["x"], s["scale"], s["mean"], s["rstd"], s["offsets"],
+                               workspace=self.ws, dx=s["dx"], dscale=s["dscale"], dshift=s["dshift"])
+
+    def prime(self):
+        for s in self.sets:                 # every copy gets its statistics
+            self.fwd(s)
+
+    def step(self, k, ev_fwd=None, ev_bwd=None):
+        sf, sb = self.sets[k % self.S], self.sets[(k + self.S // 2) % self.S]
+        if ev_fwd:
+            ev_fwd[0].record()
+        self.fwd(sf)
+        if ev_fwd:
+            ev_fwd[1].record()
+        if ev_bwd:
+            ev_bwd[0].record()
+        self.bwd(sb)
+        if ev_bwd:
+            ev_bwd[1].record()
 
 
 def main():
@@ -122,80 +195,48 @@ def main():
     import diffusion_transformer_adaln_amd as adaln
     import workloads
 
-    problems = workloads.CONFIGS[args.config]
-    if len(problems) != 1:
-        sys.exit(f"{args.config} has {len(problems)} problems; bench lines use single-problem workloads")
     torch.cuda.set_device(0)
-    pd = workloads.make_config(args.config)[0]
-    p = pd.problem
-    nbytes = workloads.algorithmic_bytes(p)
-    tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    pds = workloads.make_config(args.config)
+    runners = [Runner(pd, adaln, torch) for pd in pds]
+    nbytes = {k: sum(workloads.algorithmic_bytes(r.p)[k] for r in runners) for k in ("fwd", "bwd", "total")}
+    rows = sum(r.p.R for r in runners)
+    main_r = max(runners, key=lambda r: r.p.R * r.p.D)     # the roofline reports its backward
 
-    base = upload(pd)
-    S = 4
-    per_set = 4 * p.R * p.D * p.esize
-    while (S // 2 - 1) * per_set < (1 << 30):
-        S += 2
-    sets = []
-    for _ in range(S):
-        s = {"x": base["x"].clone(), "dy": base["dy"].clone(), "shift": base["shift"], "scale": base["scale"],
-             "offsets": base["offsets"],
-             "y": torch.empty_like(base["x"]), "dx": torch.empty_like(base["x"]),
-             "mean": torch.empty(p.R, dtype=torch.float32, device="cuda"),
-             "rstd": torch.empty(p.R, dtype=torch.float32, device="cuda"),
-             "dscale": torch.empty(p.B, p.D, dtype=tdt, device="cuda"),
-             "dshift": torch.empty(p.B, p.D, dtype=tdt, device="cuda")}
-        sets.append(s)
-    ws_bytes = adaln.adaln_bwd_workspace_size(p.B, p.R, p.D, tdt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-
-    if p.dense:
-        def fwd(s):
-            adaln.adaln_fwd(s["x"].view(p.B, p.N, p.D), s["shift"], s["scale"], p.eps,
-                            y=s["y"].view(p.B, p.N, p.D), mean=s["mean"].view(p.B, p.N),
-                            rstd=s["rstd"].view(p.B, p.N))
-
-        def bwd(s):
-            adaln.adaln_bwd(s["dy"].view(p.B, p.N, p.D), s["x"].view(p.B, p.N, p.D), s["scale"],
-                            s["mean"].view(p.B, p.N), s["rstd"].view(p.B, p.N), workspace=ws,
-                            dx=s["dx"].view(p.B, p.N, p.D), dscale=s["dscale"], dshift=s["dshift"])
-    else:
-        def fwd(s):
-            adaln.adaln_fwd_varlen(s["x"], s["shift"], s["scale"], s["offsets"], p.eps, y=s["y"],
-                                   mean=s["mean"], rstd=s["rstd"])
-
-        def bwd(s):
-            adaln.adaln_bwd_varlen(s["dy"], s["x"], s["scale"], s["mean"], s["rstd"], s["offsets"],
-                                   workspace=ws, dx=s["dx"], dscale=s["dscale"], dshift=s["dshift"])
-
-    for s in sets:                     # every copy gets its statistics
-        fwd(s)
+    for r in runners:
+        r.prime()
     for k in range(args.warmup):
-        fwd(sets[k % S])
-        bwd(sets[(k + S // 2) % S])
+        for r in runners:
+            r.step(k)
     torch.cuda.synchronize()
 
+    # Each recorded event costs a few microseconds of queue bubble, so event
+    # pairs bracket the calls of every SAMPLE-th step only: the forward on one
+    # sampled step, the backward on the next.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    SAMPLE = 5
+    ev_f = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for k in range(0, K, SAMPLE)}
+    ev_b = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for k in range(SAMPLE // 2, K, SAMPLE)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        e = ev[k]
-        e[0].record()
-        fwd(sets[k % S])
-        e[1].record()
-        bwd(sets[(k + S // 2) % S])
-        e[2].record()
+        for r in runners:
+            timed = r is main_r
+            r.step(k, ev_f.get(k) if timed else None, ev_b.get(k) if timed else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    fwd_ms = np.array([a.elapsed_time(b) for a, b in ev_f.values()])
+    bwd_ms = np.array([a.elapsed_time(b) for a, b in ev_b.values()])
     ms_per_step = wall * 1e3 / K
     gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
-    rows_per_s = p.R / (ms_per_step * 1e-3)
-    bwd_gbs = nbytes["bwd"] / (bwd_ms.mean() * 1e-3) / 1e9
-    fwd_gbs = nbytes["fwd"] / (fwd_ms.mean() * 1e-3) / 1e9
+    rows_per_s = rows / (ms_per_step * 1e-3)
+    main_bytes = workloads.algorithmic_bytes(main_r.p)
+    bwd_gbs = main_bytes["bwd"] / (bwd_ms.mean() * 1e-3) / 1e9
+    fwd_gbs = main_bytes["fwd"] / (fwd_ms.mean() * 1e-3) / 1e9
+    p = main_r.p
+    pd = main_r.pd
 
     traffic = None
     try:
@@ -219,16 +260,18 @@ def main():
         "vs_baseline": None,
         "dtype": p.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{p.name}: AdaLN fwd+bwd, B={p.B}, N={p.N if p.dense else 'ragged'}, "
-                               f"D={p.D}, R={p.R} rows, {p.dtype} I/O, fp32 statistics",
-                   "B": p.B, "rows": p.R, "D": p.D, "parallelism": "single GPU"},
+        "config": {"workload": " + ".join(
+                       f"{r.p.name}: AdaLN fwd+bwd, B={r.p.B}, N={r.p.N if r.p.dense else 'ragged'}, "
+                       f"D={r.p.D}, {r.p.dtype} I/O, fp32 statistics" for r in runners),
+                   "name": args.config, "B": sum(r.p.B for r in runners), "rows": rows,
+                   "D": p.D, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "fwd_gbs": round(fwd_gbs, 1),
         "algorithmic_bytes_per_step": nbytes["total"],
-        "roofline": {"bound": "hbm", "kernel": "adaln_bwd (row pass + finish)",
+        "roofline": {"bound": "hbm", "kernel": f"adaln_bwd on {p.name} (row pass + finish)",
                      "achieved": round(bwd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(bwd_gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
     }

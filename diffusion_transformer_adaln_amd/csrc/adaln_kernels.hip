@@ -647,24 +647,28 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // ---------------------------------------------------------------------------
 // finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
 // ---------------------------------------------------------------------------
-// Two short kernels, both with a fixed summation order (so the result is the
-// same on every run):
-//   stage 1  sample b's tiles are cut into groups of FIN_GROUP consecutive
-//            tiles; one workgroup per (group, 64-column chunk) adds the group's
-//            tiles in fp64 (slice k takes tiles k, k+SLICES, ... in ascending
-//            order; slices are then added in ascending order) and writes the
-//            fp32 result over the group's first tile.  One-tile groups are
-//            already summed and exit at once.
-//   stage 2  one workgroup per (sample, 64-column chunk) adds the sample's
-//            group sums in ascending group order in fp64 and stores dscale and
-//            dshift once, rounded to the output type.
-// Spreading stage 1 over (groups x chunks) workgroups keeps every load of the
-// partial sums in flight at once instead of walking hundreds of tiles serially.
+// Two short kernels with a fixed summation order (the result is the same on
+// every run):
+//   groups   sample b's tiles are cut into groups of FIN_GROUP consecutive
+//            tiles; one workgroup per (group, 64-column chunk) adds the
+//            group's tiles in fp64 (slice k takes tiles k, k+SLICES, ... in
+//            ascending order, then the slices are added in ascending order)
+//            and writes the fp32 group sum over the group's first tile;
+//            one-tile groups are already summed and exit at once;
+//   samples  one workgroup per (sample, 64-column chunk) adds the sample's
+//            group sums in ascending order in fp64 and stores dscale and
+//            dshift, rounded once to the output type (zeros for a sample
+//            without rows).
+// Spreading the first stage over (groups x chunks) workgroups keeps every
+// load of the partial sums in flight at once.  A single kernel with a
+// last-arriving-workgroup hand-off was measured 4x slower on MI355X: each
+// workgroup's device-scope release fence writes back its XCD's whole L2,
+// which the kernel boundary does once.
 constexpr int FIN_COLS = 64;
 constexpr int FIN_GROUP = 32;
-constexpr int FIN_SLICES = 4;
+constexpr int FIN_NT = 256;
 
-// Tiles [t0, t1) of sample b, and for stage 1 the range of group gi.
+// Tiles [t0, t1) of sample b.
 __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl, int64_t b,
                                              int64_t& t0, int64_t& t1) {
   if (rm.offsets == nullptr) {
@@ -675,6 +679,7 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
   }
 }
 
+// Tiles [t0, t1) of finish group gi; false past the last group.
 __device__ __forceinline__ bool group_tiles(const RowMap& rm, const Tiling& tl, int64_t gi,
                                             int64_t& t0, int64_t& t1) {
   int64_t b, k;
@@ -697,46 +702,162 @@ __device__ __forceinline__ bool group_tiles(const RowMap& rm, const Tiling& tl, 
   sample_tiles(rm, tl, b, s0, s1);
   t0 = s0 + k * FIN_GROUP;
   t1 = min(s1, t0 + FIN_GROUP);
-  return t1 - t0 > 1;
+  return true;
 }
 
-template <int SLICES>
-__global__ void __launch_bounds__(FIN_COLS * SLICES)
+// Column access of the finish: VEC4 lanes load 4 adjacent fp32 columns (16
+// lanes cover a 64-column chunk), scalar lanes one column (64 lanes).
+template <bool VEC4> struct FinCols {
+  static constexpr int W = VEC4 ? 4 : 1;
+  static constexpr int LANES = FIN_COLS / W;
+  static constexpr int SLICES = FIN_NT / LANES;
+  __device__ static __forceinline__ void load(const float* p, int d, int D, float* v) {
+    if constexpr (VEC4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + d);
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+      v[0] = d < D ? p[d] : 0.0f;
+    }
+  }
+};
+
+template <bool VEC4>
+__global__ void __launch_bounds__(FIN_NT)
 finish_groups_kernel(float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks) {
-  __shared__ double sh_h[SLICES][FIN_COLS];
-  __shared__ double sh_s[SLICES][FIN_COLS];
+  using C = FinCols<VEC4>;
+  constexpr int W = C::W, LANES = C::LANES, SLICES = C::SLICES;
+  __shared__ double sh_h[SLICES][LANES][W];
+  __shared__ double sh_s[SLICES][LANES][W];
   const int64_t gi = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - static_cast<int>(gi * col_blocks);
   int64_t t0, t1;
-  if (!group_tiles(rm, tl, gi, t0, t1)) return;      // whole workgroup: uniform
-  const int lane = threadIdx.x % FIN_COLS;
-  const int slice = threadIdx.x / FIN_COLS;
-  const int d = cb * FIN_COLS + lane;
+  if (!group_tiles(rm, tl, gi, t0, t1) || t1 - t0 <= 1) return;   // uniform over the workgroup
+  const int lane = threadIdx.x % LANES;
+  const int slice = threadIdx.x / LANES;
+  const int d = cb * FIN_COLS + lane * W;
   const int64_t stride = 2 * static_cast<int64_t>(D);
-  double h = 0.0, s = 0.0;
-  if (d < D) {
+
+  double h[W], sc[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) { h[w] = 0.0; sc[w] = 0.0; }
+  if (VEC4 || d < D) {
     constexpr int PER = (FIN_GROUP + SLICES - 1) / SLICES;
-    float vh[PER], vs[PER];
+    float vh[PER][W], vs[PER][W];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int64_t t = t0 + slice + u * SLICES;
-      vh[u] = t < t1 ? partial[t * stride + d] : 0.f;
-      vs[u] = t < t1 ? partial[t * stride + D + d] : 0.f;
+      if (t < t1) {
+        C::load(partial + t * stride, d, D, vh[u]);
+        C::load(partial + t * stride + D, d, D, vs[u]);
+      } else {
+#pragma unroll
+        for (int w = 0; w < W; ++w) { vh[u][w] = 0.0f; vs[u][w] = 0.0f; }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < PER; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
-  }
-  sh_h[slice][lane] = h;
-  sh_s[slice][lane] = s;
-  __syncthreads();
-  if (slice == 0 && d < D) {
-    double hh = sh_h[0][lane], ss = sh_s[0][lane];
+    for (int u = 0; u < PER; ++u)
 #pragma unroll
-    for (int k = 1; k < SLICES; ++k) { hh += sh_h[k][lane]; ss += sh_s[k][lane]; }
-    partial[t0 * stride + d] = static_cast<float>(hh);
-    partial[t0 * stride + D + d] = static_cast<float>(ss);
+      for (int w = 0; w < W; ++w) { h[w] += static_cast<double>(vh[u][w]); sc[w] += static_cast<double>(vs[u][w]); }
+  }
+#pragma unroll
+  for (int w = 0; w < W; ++w) { sh_h[slice][lane][w] = h[w]; sh_s[slice][lane][w] = sc[w]; }
+  __syncthreads();
+  if (slice == 0) {
+#pragma unroll 1
+    for (int q = 1; q < SLICES; ++q)
+#pragma unroll
+      for (int w = 0; w < W; ++w) { h[w] += sh_h[q][lane][w]; sc[w] += sh_s[q][lane][w]; }
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      if (d + w < D) {
+        partial[t0 * stride + d + w] = static_cast<float>(h[w]);
+        partial[t0 * stride + D + d + w] = static_cast<float>(sc[w]);
+      }
   }
 }
+
+// One-kernel finish for samples with at most NSLICE * PER tiles: one
+// 256-thread workgroup per (sample, COLS-column chunk).  Thread (slice,
+// lane) adds tiles slice, slice + NSLICE, ... (ascending, at most PER) for 4
+// adjacent columns; the NSLICE slice sums are then added in a fixed
+// two-level order (runs of 8 slices, then the run sums).  Narrow chunks give
+// enough workgroups to spread the loads over the whole chip, and every load
+// is issued up front, so the sum costs about one memory round trip.
+constexpr int NARROW_COLS = 16;
+constexpr int NARROW_MAX_TILES = 512;
+constexpr int NARROW_MAX_SAMPLES = 16;
+
+template <int DT, int COLS>
+__global__ void __launch_bounds__(256)
+finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D,
+                     int col_blocks, void* __restrict__ dscale, void* __restrict__ dshift) {
+  using E = Elem<DT>;
+  constexpr int LANES = COLS / 4;
+  constexpr int NSLICE = 256 / LANES;
+  constexpr int PER = 512 / NSLICE;
+  constexpr int RUNS = NSLICE / 8;
+  __shared__ float4 sl_h[NSLICE][LANES];    // per-slice sums (fp32: at most PER tiles each)
+  __shared__ float4 sl_s[NSLICE][LANES];
+  __shared__ double run_h[RUNS][LANES][4];
+  __shared__ double run_s[RUNS][LANES][4];
+  const int64_t b = blockIdx.x / col_blocks;
+  const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
+  const int lane = threadIdx.x % LANES;
+  const int slice = threadIdx.x / LANES;
+  const int d = cb * COLS + lane * 4;
+  int64_t t0, t1;
+  sample_tiles(rm, tl, b, t0, t1);
+  const int64_t stride = 2 * static_cast<int64_t>(D);
+  const bool col_ok = d < D;          // D % 4 == 0: the lane's 4 columns are all in or all out
+
+  float4 vh[PER], vs[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t t = t0 + slice + u * NSLICE;
+    if (col_ok && t < t1) {
+      vh[u] = *reinterpret_cast<const float4*>(partial + t * stride + d);
+      vs[u] = *reinterpret_cast<const float4*>(partial + t * stride + D + d);
+    } else {
+      vh[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  double h[4] = {0.0, 0.0, 0.0, 0.0}, sc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    h[0] += vh[u].x; h[1] += vh[u].y; h[2] += vh[u].z; h[3] += vh[u].w;
+    sc[0] += vs[u].x; sc[1] += vs[u].y; sc[2] += vs[u].z; sc[3] += vs[u].w;
+  }
+  sl_h[slice][lane] = make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]),
+                                  static_cast<float>(h[2]), static_cast<float>(h[3]));
+  sl_s[slice][lane] = make_float4(static_cast<float>(sc[0]), static_cast<float>(sc[1]),
+                                  static_cast<float>(sc[2]), static_cast<float>(sc[3]));
+  __syncthreads();
+  if (slice < RUNS) {
+    double a[4] = {0.0, 0.0, 0.0, 0.0}, c[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 x = sl_h[slice * 8 + q][lane], y = sl_s[slice * 8 + q][lane];
+      a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
+      c[0] += y.x; c[1] += y.y; c[2] += y.z; c[3] += y.w;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { run_h[slice][lane][w] = a[w]; run_s[slice][lane][w] = c[w]; }
+  }
+  __syncthreads();
+  if (slice == 0 && col_ok) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      double a = 0.0, c = 0.0;
+#pragma unroll
+      for (int q = 0; q < RUNS; ++q) { a += run_h[q][lane][w]; c += run_s[q][lane][w]; }
+      E::store1(dshift, b * D + d + w, static_cast<float>(a));
+      E::store1(dscale, b * D + d + w, static_cast<float>(c));
+    }
+  }
+}
+
+constexpr int FIN_UNROLL = 16;
 
 template <int DT>
 __global__ void __launch_bounds__(FIN_COLS)
@@ -752,19 +873,17 @@ finish_samples_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, i
   const int64_t stride = 2 * static_cast<int64_t>(D);
   double h = 0.0, s = 0.0;
   int64_t t = t0;
-  for (; t + 7 * FIN_GROUP < t1; t += 8 * FIN_GROUP) {
-    float vh[8], vs[8];
+  // FIN_UNROLL group sums' loads in flight, added in ascending order
+  for (; t < t1; t += FIN_UNROLL * FIN_GROUP) {
+    float vh[FIN_UNROLL], vs[FIN_UNROLL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      vh[u] = partial[(t + u * FIN_GROUP) * stride + d];
-      vs[u] = partial[(t + u * FIN_GROUP) * stride + D + d];
+    for (int u = 0; u < FIN_UNROLL; ++u) {
+      const int64_t tt = t + u * FIN_GROUP;
+      vh[u] = tt < t1 ? partial[tt * stride + d] : 0.0f;
+      vs[u] = tt < t1 ? partial[tt * stride + D + d] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
-  }
-  for (; t < t1; t += FIN_GROUP) {
-    h += static_cast<double>(partial[t * stride + d]);
-    s += static_cast<double>(partial[t * stride + D + d]);
+    for (int u = 0; u < FIN_UNROLL; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
   }
   E::store1(dshift, b * D + d, static_cast<float>(h));
   E::store1(dscale, b * D + d, static_cast<float>(s));
@@ -853,12 +972,11 @@ VecPlan plan_vec(int dtype, int64_t D, bool backward) {
     const int64_t lpr = V / vpt;
     if (lpr % 16 || lpr > VEC_MAX_NT) continue;
     VecPlan p{true, vpt, static_cast<int>(lpr), 0};
-    // threads per workgroup: a multiple of both the row lanes and the wave;
-    // forward rows shorter than 256 lanes are paired up in one workgroup,
-    // backward rows get a workgroup of their own unless they are short
+    // threads per workgroup: a multiple of both the row lanes and the wave,
+    // at least 128 (short rows share a workgroup)
     int nt = p.lpr;
     while (nt % 64) nt += p.lpr;
-    const int min_nt = backward ? 128 : 256;
+    const int min_nt = 128;
     while (nt < min_nt && nt * 2 <= VEC_MAX_NT) nt *= 2;
     if (nt > VEC_MAX_NT) continue;
     p.nt = nt;
@@ -999,12 +1117,27 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
     }
     if (e != hipSuccess) return e;
   }
+  // Few samples whose tiles fit one narrow workgroup: single-kernel finish.
+  // Otherwise (many samples, or more tiles per sample than the narrow kernel
+  // covers) the two-stage finish, whose group stage exits at once for the
+  // one-tile groups of short samples.
+  const int64_t max_tiles_per_sample = (rm.R + tl.tile_rows - 1) / tl.tile_rows;
+  if (D % 4 == 0 && rm.B <= NARROW_MAX_SAMPLES && max_tiles_per_sample <= NARROW_MAX_TILES) {
+    const int col_blocks = static_cast<int>((D + NARROW_COLS - 1) / NARROW_COLS);
+    hipLaunchKernelGGL((finish_narrow_kernel<DT, NARROW_COLS>),
+                       dim3(static_cast<unsigned>(rm.B * col_blocks)), dim3(256), 0, stream, partial,
+                       rm, tl, static_cast<int>(D), col_blocks, dscale, dshift);
+    return hipGetLastError();
+  }
   const int col_blocks = static_cast<int>((D + FIN_COLS - 1) / FIN_COLS);
   if (rm.R > 0 && tl.groups_max > 0) {
-    hipLaunchKernelGGL((finish_groups_kernel<FIN_SLICES>),
-                       dim3(static_cast<unsigned>(tl.groups_max * col_blocks)),
-                       dim3(FIN_COLS * FIN_SLICES), 0, stream, partial, rm, tl, static_cast<int>(D),
-                       col_blocks);
+    const dim3 grid(static_cast<unsigned>(tl.groups_max * col_blocks));
+    if (D % 4 == 0)
+      hipLaunchKernelGGL((finish_groups_kernel<true>), grid, dim3(FIN_NT), 0, stream, partial, rm,
+                         tl, static_cast<int>(D), col_blocks);
+    else
+      hipLaunchKernelGGL((finish_groups_kernel<false>), grid, dim3(FIN_NT), 0, stream, partial, rm,
+                         tl, static_cast<int>(D), col_blocks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL((finish_samples_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),

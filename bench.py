@@ -48,8 +48,10 @@ def parse():
     ap.add_argument("--config", default="video_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "adaln_bwd_video_bf16_traffic.txt"),
                     help="measured HBM bytes per backward call (from rocprofv3 counters), if present")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
 
 
@@ -183,8 +185,9 @@ class Runner:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(a rank's work is the one-GPU workload; see the design notes on sharding)",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path.  Under "
+              "sequence sharding each GPU runs this same one-GPU workload on its share of the "
+              "rows, and only the per-sample dscale/dshift partial sums would need a cross-GPU sum.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -238,14 +241,14 @@ def main():
     p = main_r.p
     pd = main_r.pd
 
-    traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            t = json.load(f)
-        if t.get("config") == args.config and t.get("kernel_source_sha") == kernel_source_sha():
-            traffic = t["bwd_bytes_per_call"]
-    except (OSError, ValueError, KeyError):
-        traffic = None
+    if args.copy_probe:                 # plain copy of known size, for counter calibration
+        src = torch.empty(1 << 27, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    traffic = read_traffic(args.traffic_file, args.config)
 
     out = {
         "metric": METRIC,
@@ -278,6 +281,23 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pd, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def read_traffic(path, config):
+    """HBM bytes per backward call from a committed counter summary, if it was
+    taken on this workload and on the current kernel sources (else None)."""
+    try:
+        fields = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("workload") != config or fields.get("kernel_source_sha") != kernel_source_sha():
+            return None
+        return int(fields["bwd_hbm_bytes_per_call"])
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def kernel_source_sha():

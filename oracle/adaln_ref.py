@@ -32,12 +32,16 @@ plain definition, in float64, with no fusion, blocking or reordering:
     B4  dshift[b,d] = sum over rows r of sample b of dy[r,d]
     B5  dscale[b,d] = sum over rows r of sample b of dy[r,d] * xhat[r,d]
 
-Readings where the page is silent (the modulation form (1 + scale), no LN
-affine, biased variance, eps inside the square root, per-sample [B, D]
-modulation, sums rather than means over N) are listed with their reasons in
-the repository's design notes.  B3 is the derivative of F4 for a row; it is
-pinned by finite differences and by torch's fp64 autograd in the oracle tests,
-not by retyping.
+Where the page is silent this module takes the plainest reading: the
+modulation multiplies by (1 + scale) and then adds shift (the usual AdaLN
+form, so scale = 0 is the identity); LayerNorm has no affine of its own
+(scale and shift are the only affine); the variance is the biased one
+(divide by D), as LayerNorm defines it; eps is added to the variance inside
+the square root; scale and shift are per-sample [B, D] activations broadcast
+over the sample's rows; and their gradients are sums over those rows, not
+means.  B3 is the derivative of F4 for a row; it is pinned by finite
+differences and by torch's fp64 autograd in the oracle tests, not by
+retyping.
 
 Rows belong to samples through ``offsets`` (int64, length B+1, non-decreasing,
 offsets[0] = 0, offsets[B] = R): sample b owns rows offsets[b] .. offsets[b+1]-1.

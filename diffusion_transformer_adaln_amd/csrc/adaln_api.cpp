@@ -141,10 +141,9 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
   const adaln::WorkspaceLayout wl =
       adaln::bwd_workspace_layout(B, R, D, cus, offsets != nullptr, N);
   if (workspace_bytes < wl.total) return ADALN_ERR_WORKSPACE_TOO_SMALL;
-  // one workgroup per tile; (groups or samples) x ceil(D/64) finish workgroups
-  const int64_t col_blocks = (D + 63) / 64;
-  if (wl.tiles_max > INT32_MAX || B > INT32_MAX / col_blocks || wl.groups_max > INT32_MAX / col_blocks)
-    return ADALN_ERR_UNSUPPORTED_SHAPE;
+  // one workgroup per tile; up to B * ceil(D/16) finish workgroups
+  const int64_t col_blocks = (D + 15) / 16;
+  if (wl.tiles_max > INT32_MAX || B > INT32_MAX / col_blocks) return ADALN_ERR_UNSUPPORTED_SHAPE;
 
   const Span outs[] = {{dx, s.row_bytes_total},
                        {dscale, s.mod_bytes},
@@ -158,10 +157,8 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
   const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true);
   const bool vec = vp.ok && aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(scale);
   char* ws = static_cast<char*>(workspace);
-  adaln::Tiling tl{wl.tile_rows, wl.tiles_max,
-                   offsets ? reinterpret_cast<int64_t*>(ws + wl.tile_start_off) : nullptr,
-                   offsets ? reinterpret_cast<int64_t*>(ws + wl.group_start_off) : nullptr,
-                   wl.groups_max, 1};
+  adaln::Tiling tl{wl.tile_rows, wl.tiles_max, wl.tiles_alloc,
+                   offsets ? reinterpret_cast<int64_t*>(ws + wl.tile_start_off) : nullptr, 1};
   float* partial = reinterpret_cast<float*>(ws + wl.partial_off);
   const adaln::RowMap rm{B, R, N, offsets};
   const hipError_t e = adaln::launch_bwd(dtype, dy, x, scale, mean, rstd, rm, D, vec, vp, tl,

@@ -27,9 +27,8 @@ struct RowMap {
 struct Tiling {
   int64_t tile_rows;
   int64_t tiles_max;         // grid size of the row pass (upper bound for varlen)
+  int64_t tiles_alloc;       // tile capacity of the partial-sum buffer (>= any tile count)
   int64_t* tile_start;       // device, B+1 entries (varlen only), else nullptr
-  int64_t* group_start;      // device, B+1 entries (varlen only): first finish group of each sample
-  int64_t groups_max;        // finish groups (upper bound for varlen)
   int interleave;            // 1: tile k of a sample takes rows k, k+tiles, ...; 0: contiguous runs
 };
 
@@ -58,7 +57,7 @@ hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scal
                       hipStream_t stream, void* dx, void* dscale, void* dshift);
 
 // Rows per backward tile for R rows on a device with num_cu compute units.
-int64_t bwd_tile_rows(int64_t R, int num_cu);
+int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen);
 
 // Bytes of workspace for the backward (tile table + partial sums).
 size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);
@@ -66,12 +65,11 @@ size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);
 // Layout of that workspace.
 struct WorkspaceLayout {
   size_t tile_start_off;   // int64 [B+1]
-  size_t group_start_off;  // int64 [B+1]
-  size_t partial_off;      // fp32 [tiles_max][2][D]
+  size_t partial_off;      // fp32 [ceil(D/16)][tiles_alloc][2][16]
   size_t total;
   int64_t tile_rows;
   int64_t tiles_max;
-  int64_t groups_max;
+  int64_t tiles_alloc;
 };
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense);

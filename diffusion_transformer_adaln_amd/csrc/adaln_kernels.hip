@@ -231,6 +231,16 @@ __device__ __forceinline__ void tile_rows_of(const RowMap& rm, const Tiling& tl,
   }
 }
 
+// Tile partial sums are stored chunk-major: for each 16-column chunk, the
+// tiles' 16-float rows of sum(dy) and sum(dy*xhat) follow each other, so the
+// finish reads each chunk's tiles as one contiguous run (on MI355X this cut the
+// finish from 10.0 to 6.4 us on the video shape against a tile-major layout).
+// Element (tile t, quantity q: 0 = sum dy, 1 = sum dy*xhat, column d):
+constexpr int PCOLS = 16;
+__device__ __forceinline__ int64_t pidx(int64_t tiles_alloc, int64_t t, int q, int d) {
+  return ((static_cast<int64_t>(d / PCOLS) * tiles_alloc + t) * 2 + q) * PCOLS + (d % PCOLS);
+}
+
 // Largest workgroup of the vectorised kernels: 8 waves, i.e. two per SIMD, so
 // the compiler may give each wave up to 256 VGPRs.
 constexpr int VEC_MAX_NT = 512;
@@ -375,7 +385,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // Grid: one workgroup per tile (a run of rows inside one sample).
 // LDS: 2 buffers x [slots][RIF][groups] x (sum g, sum g*xhat), then, when a
 // workgroup holds several slots, [2][D] floats for the slot combine.
-template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool PF = true>
+template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool PF = true, bool OPAQUE = false>
 __global__ void __launch_bounds__(NTMAX)
 bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
                const uint4* __restrict__ scale, const float* __restrict__ mean,
@@ -487,6 +497,18 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       }
     }
 
+    if (OPAQUE) {
+      // Hide the packed rows from the optimiser here, so the output pass
+      // unpacks them again instead of keeping the first pass's fp32 copies
+      // alive across the reduction (fewer VGPRs, more waves per SIMD).
+#pragma unroll
+      for (int i = 0; i < RIF; ++i)
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          asm volatile("" : "+v"(xv[i][j].x), "+v"(xv[i][j].y), "+v"(xv[i][j].z), "+v"(xv[i][j].w));
+          asm volatile("" : "+v"(gv[i][j].x), "+v"(gv[i][j].y), "+v"(gv[i][j].z), "+v"(gv[i][j].w));
+        }
+    }
 #pragma unroll
     for (int i = 0; i < RIF; ++i) {
       const int64_t m = base + static_cast<int64_t>(slot) * RIF + i;
@@ -520,17 +542,18 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
     }
   }
 
-  // tile partials: partial[t][0][:] = sum dy, partial[t][1][:] = sum dy*xhat
-  float* ph = partial + t * 2 * static_cast<int64_t>(D);
-  float* ps = ph + D;
+  // tile partials, chunk-major (see pidx)
+  const int64_t TA = tl.tiles_alloc;
   if (nslots == 1) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int col = (j * lpr + lane) * EPV;
 #pragma unroll
       for (int k = 0; k < EPV; k += 4) {
-        *reinterpret_cast<float4*>(ph + col + k) = make_float4(acc_h[j][k], acc_h[j][k + 1], acc_h[j][k + 2], acc_h[j][k + 3]);
-        *reinterpret_cast<float4*>(ps + col + k) = make_float4(acc_s[j][k], acc_s[j][k + 1], acc_s[j][k + 2], acc_s[j][k + 3]);
+        *reinterpret_cast<float4*>(partial + pidx(TA, t, 0, col + k)) =
+            make_float4(acc_h[j][k], acc_h[j][k + 1], acc_h[j][k + 2], acc_h[j][k + 3]);
+        *reinterpret_cast<float4*>(partial + pidx(TA, t, 1, col + k)) =
+            make_float4(acc_s[j][k], acc_s[j][k + 1], acc_s[j][k + 2], acc_s[j][k + 3]);
       }
     }
   } else {
@@ -550,8 +573,12 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       }
       __syncthreads();
     }
-    for (int c = tid * 4; c < 2 * D; c += blockDim.x * 4)
-      *reinterpret_cast<float4*>(ph + c) = *reinterpret_cast<const float4*>(comb + c);
+    const int d4 = D / 4;
+    for (int i = tid; i < 2 * d4; i += blockDim.x) {
+      const int q = i / d4, col = (i - q * d4) * 4;
+      *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) =
+          *reinterpret_cast<const float4*>(comb + q * D + col);
+    }
   }
 }
 
@@ -616,9 +643,11 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
   if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;
   int64_t b, first, step, count;
   tile_rows_of(rm, tl, t, b, first, step, count);
-  float* ph = partial + t * 2 * static_cast<int64_t>(D);
-  float* ps = ph + D;
-  for (int d = threadIdx.x; d < D; d += GEN_NT) { ph[d] = 0.f; ps[d] = 0.f; }
+  const int64_t TA = tl.tiles_alloc;
+  for (int d = threadIdx.x; d < D; d += GEN_NT) {
+    partial[pidx(TA, t, 0, d)] = 0.f;
+    partial[pidx(TA, t, 1, d)] = 0.f;
+  }
   const float inv_d = 1.0f / static_cast<float>(D);
   int k = 0;
   for (int64_t m = 0; m < count; ++m) {
@@ -638,8 +667,8 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
       const float gy = E::load1(dy, base + d);
       const float g = mul_rounded(gy, 1.0f + E::load1(scale, b * D + d));
       E::store1(dx, base + d, rs * ((g - a) - xh * c));
-      ph[d] += gy;
-      ps[d] += gy * xh;
+      partial[pidx(TA, t, 0, d)] += gy;
+      partial[pidx(TA, t, 1, d)] += gy * xh;
     }
   }
 }
@@ -647,26 +676,13 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // ---------------------------------------------------------------------------
 // finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
 // ---------------------------------------------------------------------------
-// Two short kernels with a fixed summation order (the result is the same on
-// every run):
-//   groups   sample b's tiles are cut into groups of FIN_GROUP consecutive
-//            tiles; one workgroup per (group, 64-column chunk) adds the
-//            group's tiles in fp64 (slice k takes tiles k, k+SLICES, ... in
-//            ascending order, then the slices are added in ascending order)
-//            and writes the fp32 group sum over the group's first tile;
-//            one-tile groups are already summed and exit at once;
-//   samples  one workgroup per (sample, 64-column chunk) adds the sample's
-//            group sums in ascending order in fp64 and stores dscale and
-//            dshift, rounded once to the output type (zeros for a sample
-//            without rows).
-// Spreading the first stage over (groups x chunks) workgroups keeps every
-// load of the partial sums in flight at once.  A single kernel with a
-// last-arriving-workgroup hand-off was measured 4x slower on MI355X: each
-// workgroup's device-scope release fence writes back its XCD's whole L2,
-// which the kernel boundary does once.
-constexpr int FIN_COLS = 64;
-constexpr int FIN_GROUP = 32;
-constexpr int FIN_NT = 256;
+// Both variants add the tiles in an order fixed by the shape and the CU count
+// alone, in fp64, and round once to the output type: bitwise repeatable, no
+// atomics.  Measured alternatives on MI355X (video shape) and why they lost:
+// one thread walking all tiles of its column (49 us, latency-bound); a
+// cooperative grid sync (about 30 us per sync); a last-arriving-workgroup
+// hand-off inside one kernel (46 us: each workgroup's device-scope release
+// fence writes back its XCD's L2); groups-then-samples in two kernels (13 us).
 
 // Tiles [t0, t1) of sample b.
 __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl, int64_t b,
@@ -679,122 +695,24 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
   }
 }
 
-// Tiles [t0, t1) of finish group gi; false past the last group.
-__device__ __forceinline__ bool group_tiles(const RowMap& rm, const Tiling& tl, int64_t gi,
-                                            int64_t& t0, int64_t& t1) {
-  int64_t b, k;
-  if (rm.offsets == nullptr) {
-    const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
-    const int64_t gps = (tps + FIN_GROUP - 1) / FIN_GROUP;
-    if (gps == 0) return false;
-    b = gi / gps; k = gi - b * gps;
-    if (b >= rm.B) return false;
-  } else {
-    if (gi >= tl.group_start[rm.B]) return false;
-    int64_t lo = 0, hi = rm.B;     // largest b with group_start[b] <= gi
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (tl.group_start[mid] <= gi) lo = mid; else hi = mid;
-    }
-    b = lo; k = gi - tl.group_start[b];
-  }
-  int64_t s0, s1;
-  sample_tiles(rm, tl, b, s0, s1);
-  t0 = s0 + k * FIN_GROUP;
-  t1 = min(s1, t0 + FIN_GROUP);
-  return true;
-}
-
-// Column access of the finish: VEC4 lanes load 4 adjacent fp32 columns (16
-// lanes cover a 64-column chunk), scalar lanes one column (64 lanes).
-template <bool VEC4> struct FinCols {
-  static constexpr int W = VEC4 ? 4 : 1;
-  static constexpr int LANES = FIN_COLS / W;
-  static constexpr int SLICES = FIN_NT / LANES;
-  __device__ static __forceinline__ void load(const float* p, int d, int D, float* v) {
-    if constexpr (VEC4) {
-      const float4 f = *reinterpret_cast<const float4*>(p + d);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else {
-      v[0] = d < D ? p[d] : 0.0f;
-    }
-  }
-};
-
-template <bool VEC4>
-__global__ void __launch_bounds__(FIN_NT)
-finish_groups_kernel(float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks) {
-  using C = FinCols<VEC4>;
-  constexpr int W = C::W, LANES = C::LANES, SLICES = C::SLICES;
-  __shared__ double sh_h[SLICES][LANES][W];
-  __shared__ double sh_s[SLICES][LANES][W];
-  const int64_t gi = blockIdx.x / col_blocks;
-  const int cb = blockIdx.x - static_cast<int>(gi * col_blocks);
-  int64_t t0, t1;
-  if (!group_tiles(rm, tl, gi, t0, t1) || t1 - t0 <= 1) return;   // uniform over the workgroup
-  const int lane = threadIdx.x % LANES;
-  const int slice = threadIdx.x / LANES;
-  const int d = cb * FIN_COLS + lane * W;
-  const int64_t stride = 2 * static_cast<int64_t>(D);
-
-  double h[W], sc[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) { h[w] = 0.0; sc[w] = 0.0; }
-  if (VEC4 || d < D) {
-    constexpr int PER = (FIN_GROUP + SLICES - 1) / SLICES;
-    float vh[PER][W], vs[PER][W];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int64_t t = t0 + slice + u * SLICES;
-      if (t < t1) {
-        C::load(partial + t * stride, d, D, vh[u]);
-        C::load(partial + t * stride + D, d, D, vs[u]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < W; ++w) { vh[u][w] = 0.0f; vs[u][w] = 0.0f; }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-#pragma unroll
-      for (int w = 0; w < W; ++w) { h[w] += static_cast<double>(vh[u][w]); sc[w] += static_cast<double>(vs[u][w]); }
-  }
-#pragma unroll
-  for (int w = 0; w < W; ++w) { sh_h[slice][lane][w] = h[w]; sh_s[slice][lane][w] = sc[w]; }
-  __syncthreads();
-  if (slice == 0) {
-#pragma unroll 1
-    for (int q = 1; q < SLICES; ++q)
-#pragma unroll
-      for (int w = 0; w < W; ++w) { h[w] += sh_h[q][lane][w]; sc[w] += sh_s[q][lane][w]; }
-#pragma unroll
-    for (int w = 0; w < W; ++w)
-      if (d + w < D) {
-        partial[t0 * stride + d + w] = static_cast<float>(h[w]);
-        partial[t0 * stride + D + d + w] = static_cast<float>(sc[w]);
-      }
-  }
-}
-
-// One-kernel finish for samples with at most NSLICE * PER tiles: one
-// 256-thread workgroup per (sample, COLS-column chunk).  Thread (slice,
-// lane) adds tiles slice, slice + NSLICE, ... (ascending, at most PER) for 4
-// adjacent columns; the NSLICE slice sums are then added in a fixed
-// two-level order (runs of 8 slices, then the run sums).  Narrow chunks give
-// enough workgroups to spread the loads over the whole chip, and every load
-// is issued up front, so the sum costs about one memory round trip.
-constexpr int NARROW_COLS = 16;
-constexpr int NARROW_MAX_TILES = 512;
+// Few samples, at most NARROW_MAX_TILES tiles each: one 256-thread workgroup
+// per (sample, 16-column chunk).  Thread (slice, lane) adds tiles slice,
+// slice + 64, ... (ascending, at most 8) for 4 adjacent columns; the 64 slice
+// sums are then added in a fixed two-level order (8 runs of 8 slices, then the
+// run sums).  320 workgroups on the video shape, every load issued up front
+// over one contiguous run of partials: about one memory round trip.
+constexpr int NARROW_LANES = PCOLS / 4;                  // float4 lanes per chunk
+constexpr int NARROW_SLICES = 256 / NARROW_LANES;        // 64
+constexpr int NARROW_PER = 8;                            // tiles per slice
+constexpr int NARROW_MAX_TILES = NARROW_SLICES * NARROW_PER;
 constexpr int NARROW_MAX_SAMPLES = 16;
 
-template <int DT, int COLS>
+template <int DT>
 __global__ void __launch_bounds__(256)
 finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D,
                      int col_blocks, void* __restrict__ dscale, void* __restrict__ dshift) {
   using E = Elem<DT>;
-  constexpr int LANES = COLS / 4;
-  constexpr int NSLICE = 256 / LANES;
-  constexpr int PER = 512 / NSLICE;
+  constexpr int LANES = NARROW_LANES, NSLICE = NARROW_SLICES, PER = NARROW_PER;
   constexpr int RUNS = NSLICE / 8;
   __shared__ float4 sl_h[NSLICE][LANES];    // per-slice sums (fp32: at most PER tiles each)
   __shared__ float4 sl_s[NSLICE][LANES];
@@ -804,19 +722,19 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
   const int lane = threadIdx.x % LANES;
   const int slice = threadIdx.x / LANES;
-  const int d = cb * COLS + lane * 4;
+  const int d = cb * PCOLS + lane * 4;
   int64_t t0, t1;
   sample_tiles(rm, tl, b, t0, t1);
-  const int64_t stride = 2 * static_cast<int64_t>(D);
   const bool col_ok = d < D;          // D % 4 == 0: the lane's 4 columns are all in or all out
+  const float* base = partial + pidx(tl.tiles_alloc, 0, 0, cb * PCOLS) + lane * 4;
 
   float4 vh[PER], vs[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int64_t t = t0 + slice + u * NSLICE;
     if (col_ok && t < t1) {
-      vh[u] = *reinterpret_cast<const float4*>(partial + t * stride + d);
-      vs[u] = *reinterpret_cast<const float4*>(partial + t * stride + D + d);
+      vh[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS);
+      vs[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS + PCOLS);
     } else {
       vh[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       vs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -857,81 +775,92 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   }
 }
 
-constexpr int FIN_UNROLL = 16;
+// Any number of samples and tiles, any D: one 256-thread workgroup per
+// (sample, 64 columns); slice k adds tiles k, k+4, ... in ascending order
+// (8 loads in flight per thread), then the 4 slices are added in ascending
+// order.  Used for many-sample packed batches, whose samples have few tiles.
+constexpr int TILES_COLS = 64;
+constexpr int TILES_SLICES = 4;
 
 template <int DT>
-__global__ void __launch_bounds__(FIN_COLS)
-finish_samples_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D,
-                      int col_blocks, void* __restrict__ dscale, void* __restrict__ dshift) {
+__global__ void __launch_bounds__(TILES_COLS * TILES_SLICES)
+finish_tiles_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int D, int col_blocks,
+                    void* __restrict__ dscale, void* __restrict__ dshift) {
   using E = Elem<DT>;
+  __shared__ double sh_h[TILES_SLICES][TILES_COLS];
+  __shared__ double sh_s[TILES_SLICES][TILES_COLS];
   const int64_t b = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
-  const int d = cb * FIN_COLS + threadIdx.x;
-  if (d >= D) return;
+  const int lane = threadIdx.x % TILES_COLS;
+  const int slice = threadIdx.x / TILES_COLS;
+  const int d = cb * TILES_COLS + lane;
   int64_t t0, t1;
   sample_tiles(rm, tl, b, t0, t1);
-  const int64_t stride = 2 * static_cast<int64_t>(D);
+  const int64_t TA = tl.tiles_alloc;
   double h = 0.0, s = 0.0;
-  int64_t t = t0;
-  // FIN_UNROLL group sums' loads in flight, added in ascending order
-  for (; t < t1; t += FIN_UNROLL * FIN_GROUP) {
-    float vh[FIN_UNROLL], vs[FIN_UNROLL];
+  if (d < D) {
+    const float* ph = partial + pidx(TA, 0, 0, d);     // tile t at ph[t * 2 * PCOLS]
+    int64_t t = t0 + slice;
+    for (; t + 7 * TILES_SLICES < t1; t += 8 * TILES_SLICES) {
+      float vh[8], vs[8];
 #pragma unroll
-    for (int u = 0; u < FIN_UNROLL; ++u) {
-      const int64_t tt = t + u * FIN_GROUP;
-      vh[u] = tt < t1 ? partial[tt * stride + d] : 0.0f;
-      vs[u] = tt < t1 ? partial[tt * stride + D + d] : 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        vh[u] = ph[(t + u * TILES_SLICES) * 2 * PCOLS];
+        vs[u] = ph[(t + u * TILES_SLICES) * 2 * PCOLS + PCOLS];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
     }
-#pragma unroll
-    for (int u = 0; u < FIN_UNROLL; ++u) { h += static_cast<double>(vh[u]); s += static_cast<double>(vs[u]); }
+    for (; t < t1; t += TILES_SLICES) {
+      h += static_cast<double>(ph[t * 2 * PCOLS]);
+      s += static_cast<double>(ph[t * 2 * PCOLS + PCOLS]);
+    }
   }
-  E::store1(dshift, b * D + d, static_cast<float>(h));
-  E::store1(dscale, b * D + d, static_cast<float>(s));
+  sh_h[slice][lane] = h;
+  sh_s[slice][lane] = s;
+  __syncthreads();
+  if (slice == 0 && d < D) {
+#pragma unroll
+    for (int k = 1; k < TILES_SLICES; ++k) { h += sh_h[k][lane]; s += sh_s[k][lane]; }
+    E::store1(dshift, b * D + d, static_cast<float>(h));
+    E::store1(dscale, b * D + d, static_cast<float>(s));
+  }
 }
 
 // ---------------------------------------------------------------------------
-// varlen prologue: tile_start[b]  = sum_{c<b} ceil(rows_c / tile_rows)
-//                  group_start[b] = sum_{c<b} ceil(tiles_c / FIN_GROUP)
+// varlen prologue: tile_start[b] = sum_{c<b} ceil(rows_c / tile_rows)
 // ---------------------------------------------------------------------------
 constexpr int PRO_NT = 1024;
 
 __global__ void __launch_bounds__(PRO_NT)
 varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile_rows,
-                    int64_t* __restrict__ tile_start, int64_t* __restrict__ group_start) {
-  __shared__ int64_t scan_t[PRO_NT];
-  __shared__ int64_t scan_g[PRO_NT];
-  __shared__ int64_t carry_t, carry_g;
-  if (threadIdx.x == 0) { carry_t = 0; carry_g = 0; }
+                    int64_t* __restrict__ tile_start) {
+  __shared__ int64_t scan[PRO_NT];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
   __syncthreads();
   for (int64_t base = 0; base < B; base += PRO_NT) {
     const int64_t b = base + threadIdx.x;
-    int64_t ct = 0, cg = 0;
+    int64_t cnt = 0;
     if (b < B) {
       const int64_t n = offsets[b + 1] - offsets[b];
-      ct = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
-      cg = (ct + FIN_GROUP - 1) / FIN_GROUP;
+      cnt = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
     }
-    scan_t[threadIdx.x] = ct;
-    scan_g[threadIdx.x] = cg;
+    scan[threadIdx.x] = cnt;
     __syncthreads();
-    // Hillis-Steele inclusive scans over the chunk
+    // Hillis-Steele inclusive scan over the chunk
     for (int off = 1; off < PRO_NT; off <<= 1) {
-      const int64_t vt = threadIdx.x >= off ? scan_t[threadIdx.x - off] : 0;
-      const int64_t vg = threadIdx.x >= off ? scan_g[threadIdx.x - off] : 0;
+      const int64_t v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
       __syncthreads();
-      scan_t[threadIdx.x] += vt;
-      scan_g[threadIdx.x] += vg;
+      scan[threadIdx.x] += v;
       __syncthreads();
     }
-    if (b < B) {
-      tile_start[b] = carry_t + scan_t[threadIdx.x] - ct;   // exclusive
-      group_start[b] = carry_g + scan_g[threadIdx.x] - cg;
-    }
+    if (b < B) tile_start[b] = carry + scan[threadIdx.x] - cnt;   // exclusive
     __syncthreads();
-    if (threadIdx.x == PRO_NT - 1) { carry_t += scan_t[PRO_NT - 1]; carry_g += scan_g[PRO_NT - 1]; }
+    if (threadIdx.x == PRO_NT - 1) carry += scan[PRO_NT - 1];
     __syncthreads();
   }
-  if (threadIdx.x == 0) { tile_start[B] = carry_t; group_start[B] = carry_g; }
+  if (threadIdx.x == 0) tile_start[B] = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -988,15 +917,22 @@ VecPlan plan_vec(int dtype, int64_t D, bool backward) {
   return best;
 }
 
-// Backward tiles per compute unit (a tile's column partials cost 8*D bytes
-// written and read again, so fewer, longer tiles are cheaper; two per CU
-// measured best), and the forward's workgroup count per CU (many short-lived
-// workgroups keep the rows in flight inside a narrow window of memory).
+// Backward tiles per compute unit for dense batches (a tile's column partials
+// cost 8*D bytes written and read again, so fewer, longer tiles are cheaper;
+// two per CU measured best on the video shape), and the forward's workgroup
+// count per CU (many short-lived workgroups keep the rows in flight inside a
+// narrow window of memory).
 constexpr int BWD_TILES_PER_CU = 2;
+// Packed batches mix short and long samples, so their tiles vary in length;
+// four tiles per CU lets the workgroup dispatcher even out the load (mixed
+// 256..32760-row samples at D = 3072: 952 us at two per CU, 907 at four, 927
+// at eight).
+constexpr int BWD_VARLEN_TILES_PER_CU = 4;
 constexpr int FWD_WG_PER_CU = 32;
 
-int64_t bwd_tile_rows(int64_t R, int num_cu) {
-  const int64_t target = static_cast<int64_t>(num_cu) * BWD_TILES_PER_CU;
+int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen) {
+  const int64_t target =
+      static_cast<int64_t>(num_cu) * (varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU);
   return R <= 0 ? 1 : (R + target - 1) / target;
 }
 
@@ -1005,25 +941,24 @@ static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255);
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense) {
   WorkspaceLayout w{};
-  w.tile_rows = bwd_tile_rows(R, num_cu);
-  const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;
-  if (varlen) {
-    w.tiles_max = bound;
-    w.groups_max = (bound + FIN_GROUP - 1) / FIN_GROUP + B;
-  } else {
-    const int64_t tps = (N_dense + w.tile_rows - 1) / w.tile_rows;
-    w.tiles_max = B * tps;
-    w.groups_max = B * ((tps + FIN_GROUP - 1) / FIN_GROUP);
-  }
+  w.tile_rows = bwd_tile_rows(R, num_cu, varlen);
+  const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;   // tiles of any row split
+  w.tiles_alloc = bound;
+  w.tiles_max = varlen ? bound : B * ((N_dense + w.tile_rows - 1) / w.tile_rows);
   w.tile_start_off = 0;
-  w.group_start_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
-  w.partial_off = w.group_start_off + align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
-  w.total = w.partial_off + static_cast<size_t>(bound) * 2 * static_cast<size_t>(D) * sizeof(float);
+  w.partial_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
+  const int64_t chunks = (D + PCOLS - 1) / PCOLS;
+  w.total = w.partial_off +
+            static_cast<size_t>(chunks) * static_cast<size_t>(bound) * 2 * PCOLS * sizeof(float);
   return w;
 }
 
+// Enough for either entry point: the packed layout's tile bound covers any
+// row split, and the dense one is checked as well in case its tiles are finer.
 size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu) {
-  return bwd_workspace_layout(B, R, D, num_cu, true, 0).total;
+  const size_t packed = bwd_workspace_layout(B, R, D, num_cu, true, 0).total;
+  const size_t dense = bwd_workspace_layout(B, R, D, num_cu, false, B > 0 ? R / B : 0).total;
+  return packed > dense ? packed : dense;
 }
 
 template <int DT, int VPT>
@@ -1097,7 +1032,7 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
   hipError_t e = hipSuccess;
   if (rm.offsets != nullptr) {
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       tl.tile_rows, tl.tile_start, tl.group_start);
+                       tl.tile_rows, tl.tile_start);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rm.R > 0 && tl.tiles_max > 0) {
@@ -1117,32 +1052,20 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
     }
     if (e != hipSuccess) return e;
   }
-  // Few samples whose tiles fit one narrow workgroup: single-kernel finish.
-  // Otherwise (many samples, or more tiles per sample than the narrow kernel
-  // covers) the two-stage finish, whose group stage exits at once for the
-  // one-tile groups of short samples.
+  // finish: the narrow kernel for few samples whose tiles fit one workgroup,
+  // else one workgroup per (sample, 64 columns)
   const int64_t max_tiles_per_sample = (rm.R + tl.tile_rows - 1) / tl.tile_rows;
   if (D % 4 == 0 && rm.B <= NARROW_MAX_SAMPLES && max_tiles_per_sample <= NARROW_MAX_TILES) {
-    const int col_blocks = static_cast<int>((D + NARROW_COLS - 1) / NARROW_COLS);
-    hipLaunchKernelGGL((finish_narrow_kernel<DT, NARROW_COLS>),
-                       dim3(static_cast<unsigned>(rm.B * col_blocks)), dim3(256), 0, stream, partial,
-                       rm, tl, static_cast<int>(D), col_blocks, dscale, dshift);
-    return hipGetLastError();
+    const int col_blocks = static_cast<int>((D + PCOLS - 1) / PCOLS);
+    hipLaunchKernelGGL((finish_narrow_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),
+                       dim3(256), 0, stream, partial, rm, tl, static_cast<int>(D), col_blocks,
+                       dscale, dshift);
+  } else {
+    const int col_blocks = static_cast<int>((D + TILES_COLS - 1) / TILES_COLS);
+    hipLaunchKernelGGL((finish_tiles_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),
+                       dim3(TILES_COLS * TILES_SLICES), 0, stream, partial, rm, tl,
+                       static_cast<int>(D), col_blocks, dscale, dshift);
   }
-  const int col_blocks = static_cast<int>((D + FIN_COLS - 1) / FIN_COLS);
-  if (rm.R > 0 && tl.groups_max > 0) {
-    const dim3 grid(static_cast<unsigned>(tl.groups_max * col_blocks));
-    if (D % 4 == 0)
-      hipLaunchKernelGGL((finish_groups_kernel<true>), grid, dim3(FIN_NT), 0, stream, partial, rm,
-                         tl, static_cast<int>(D), col_blocks);
-    else
-      hipLaunchKernelGGL((finish_groups_kernel<false>), grid, dim3(FIN_NT), 0, stream, partial, rm,
-                         tl, static_cast<int>(D), col_blocks);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((finish_samples_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),
-                     dim3(FIN_COLS), 0, stream, partial, rm, tl, static_cast<int>(D), col_blocks,
-                     dscale, dshift);
   return hipGetLastError();
 }
 

@@ -174,13 +174,18 @@ def test_run_to_run_bitwise(dtype, D, lengths):
 
 
 @pytest.mark.parametrize("dtype,D,N,B", [("bf16", 3072, 515, 3), ("f32", 128, 300, 2), ("bf16", 100, 33, 2)])
-def test_dense_equals_packed_bitwise(dtype, D, N, B):
+def test_dense_and_packed_agree(dtype, D, N, B):
+    """Row outputs are computed identically by both entry points (bitwise);
+    the column sums may group tiles differently (packed batches use shorter
+    tiles), so they must agree to the accuracy contract."""
     pd = _pd(dtype, D, [N] * B, seed=31)
-    say(f"[dense==packed] {dtype} D={D} N={N} B={B}")
+    say(f"[dense vs packed] {dtype} D={D} N={N} B={B}")
     a = run_gpu(pd, dense=True)
     b = run_gpu(pd, dense=False)
-    for k in a:
+    for k in ("y", "mean", "rstd", "dx"):
         assert bits(a[k]) == bits(b[k]), k
+    check_all(pd, a)
+    check_all(pd, b)
 
 
 # ---------------------------------------------------------------------------

@@ -94,6 +94,24 @@ template <> struct Elem<BF16> {
   }
 };
 
+// Streaming (non-temporal) 16-byte accesses for the row tensors of the
+// vectorised kernels: x, dy, y and dx are touched once per call and are far
+// larger than L2 plus the MALL, so caching them buys nothing.  Measured on
+// MI355X (video shape, fwd and bwd alternating on cold buffers): streaming
+// loads take the backward row pass from 128 to 107 us, and streaming stores
+// leave no dirty lines for the next kernel to write back (a following
+// backward runs 117 instead of 128 us).  The general kernels re-read a row
+// from cache and keep ordinary accesses.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Product rounded to fp32 on its own: never fused into a following add, so a
 // value computed twice (once for a row sum, once for the output) has the
 // same bits both times.
@@ -299,7 +317,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
       valid[i] = row[i] < r_end;
       const uint4* xr = x + row[i] * V + lane;
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) xv[i][j] = valid[i] ? xr[j * lpr] : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < VPT; ++j) xv[i][j] = valid[i] ? load_stream(xr + j * lpr) : make_uint4(0, 0, 0, 0);
     }
 
     // per-lane two-pass (mean, M2), then the fixed-order merge across lanes
@@ -373,7 +391,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
           const float xh = (f[k] - m[i]) * rs;      // (x - mean) * rstd
           f[k] = xh * sc1[j][k] + sh[j][k];
         }
-        yr[j * lpr] = E::pack(f);
+        store_stream(yr + j * lpr, E::pack(f));
       }
     }
   }
@@ -443,7 +461,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       const uint4* xr = x + rr * V + lane;
       const uint4* gr = dy + rr * V + lane;
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) { xa[i][j] = xr[j * lpr]; ga[i][j] = gr[j * lpr]; }
+      for (int j = 0; j < VPT; ++j) { xa[i][j] = load_stream(xr + j * lpr); ga[i][j] = load_stream(gr + j * lpr); }
     }
   };
 
@@ -529,7 +547,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
           acc_h[j][k] += fg[k];
           acc_s[j][k] += fg[k] * xh;
         }
-        dxr[j * lpr] = E::pack(out);
+        store_stream(dxr + j * lpr, E::pack(out));
       }
     }
     if (PF) {
@@ -917,18 +935,23 @@ VecPlan plan_vec(int dtype, int64_t D, bool backward) {
   return best;
 }
 
-// Backward tiles per compute unit for dense batches (a tile's column partials
+// Backward tiles per compute unit for dense batches: a tile's column partials
 // cost 8*D bytes written and read again, so fewer, longer tiles are cheaper;
-// two per CU measured best on the video shape), and the forward's workgroup
-// count per CU (many short-lived workgroups keep the rows in flight inside a
-// narrow window of memory).
+// two per CU measured best on the video shape (one: 150 us, three: 159 us,
+// two: 107 us).
 constexpr int BWD_TILES_PER_CU = 2;
 // Packed batches mix short and long samples, so their tiles vary in length;
 // four tiles per CU lets the workgroup dispatcher even out the load (mixed
 // 256..32760-row samples at D = 3072: 952 us at two per CU, 907 at four, 927
 // at eight).
 constexpr int BWD_VARLEN_TILES_PER_CU = 4;
-constexpr int FWD_WG_PER_CU = 32;
+// Forward grid: many short-lived workgroups keep the rows in flight inside a
+// narrow window of memory; about 128 per CU, but at least two iterations each
+// (measured with streaming accesses: video shape 73 us at two rows per
+// workgroup against 76 at one; mixed-length batch at D = 3072 498 us at 128
+// per CU against 514 at 64 and 540 at 32).
+constexpr int FWD_WG_PER_CU = 128;
+constexpr int FWD_MIN_ITERS = 2;
 
 int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen) {
   const int64_t target =
@@ -974,6 +997,7 @@ static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* s
   const int64_t target = static_cast<int64_t>(num_cu) * FWD_WG_PER_CU;
   int64_t rows_per_wg = (rm.R + target - 1) / target;
   rows_per_wg = ((rows_per_wg + per_iter - 1) / per_iter) * per_iter;
+  if (rows_per_wg < FWD_MIN_ITERS * per_iter) rows_per_wg = FWD_MIN_ITERS * per_iter;
   const int64_t grid = (rm.R + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL((fwd_vec_kernel<DT, VPT, RIF>), dim3(static_cast<unsigned>(grid)),
                      dim3(vp.nt), lds, stream, static_cast<const uint4*>(x),

@@ -22,6 +22,10 @@ events recorded on the launch stream inside the timed region (around every
 fifth step's calls: each event adds a few microseconds of queue bubble).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
+
+`--bwd twopass` runs the backward through adaln_bwd_twopass instead (dx
+pass, then a separate D-tile column pass that reads dy and x again): the
+same work with more traffic, to measure what the fusion saves.
 """
 
 from __future__ import annotations
@@ -50,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "adaln_bwd_video_bf16_traffic.txt"),
                     help="measured HBM bytes per backward call (from rocprofv3 counters), if present")
+    ap.add_argument("--bwd", choices=("fused", "twopass"), default="fused",
+                    help="backward entry point: the fused adaln_bwd, or adaln_bwd_twopass (dx pass, then "
+                         "a separate D-tile column pass that reads dy and x again; dense workloads only)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -121,9 +128,12 @@ class Runner:
     (k + S/2) % S; S is large enough that about 1 GB of other traffic
     separates two touches of the same copy."""
 
-    def __init__(self, pd, adaln, torch):
+    def __init__(self, pd, adaln, torch, bwd_impl="fused"):
         self.pd, self.p, self.adaln, self.torch = pd, pd.problem, adaln, torch
         p = self.p
+        if bwd_impl == "twopass" and not p.dense:
+            raise SystemExit(f"--bwd twopass takes dense workloads; {p.name} is packed")
+        self.bwd_fn = adaln.adaln_bwd_twopass if bwd_impl == "twopass" else adaln.adaln_bwd
         tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
         base = upload(pd)
         S = 4
@@ -157,7 +167,7 @@ class Runner:
     def bwd(self, s):
         p, a = self.p, self.adaln
         if p.dense:
-            a.adaln_bwd(s["dy"].view(p.B, p.N, p.D), s["x"].view(p.B, p.N, p.D), s["scale"],
+            self.bwd_fn(s["dy"].view(p.B, p.N, p.D), s["x"].view(p.B, p.N, p.D), s["scale"],
                         s["mean"].view(p.B, p.N), s["rstd"].view(p.B, p.N), workspace=self.ws,
                         dx=s["dx"].view(p.B, p.N, p.D), dscale=s["dscale"], dshift=s["dshift"])
         else:
@@ -200,7 +210,7 @@ def main():
 
     torch.cuda.set_device(0)
     pds = workloads.make_config(args.config)
-    runners = [Runner(pd, adaln, torch) for pd in pds]
+    runners = [Runner(pd, adaln, torch, args.bwd) for pd in pds]
     nbytes = {k: sum(workloads.algorithmic_bytes(r.p)[k] for r in runners) for k in ("fwd", "bwd", "total")}
     rows = sum(r.p.R for r in runners)
     main_r = max(runners, key=lambda r: r.p.R * r.p.D)     # the roofline reports its backward
@@ -248,7 +258,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    traffic = read_traffic(args.traffic_file, args.config)
+    traffic = read_traffic(args.traffic_file, args.config) if args.bwd == "fused" else None
+    bwd_name = "adaln_bwd" if args.bwd == "fused" else "adaln_bwd_twopass"
 
     out = {
         "metric": METRIC,
@@ -267,14 +278,14 @@ def main():
                        f"{r.p.name}: AdaLN fwd+bwd, B={r.p.B}, N={r.p.N if r.p.dense else 'ragged'}, "
                        f"D={r.p.D}, {r.p.dtype} I/O, fp32 statistics" for r in runners),
                    "name": args.config, "B": sum(r.p.B for r in runners), "rows": rows,
-                   "D": p.D, "parallelism": "single GPU"},
+                   "D": p.D, "bwd": bwd_name, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "fwd_gbs": round(fwd_gbs, 1),
         "algorithmic_bytes_per_step": nbytes["total"],
-        "roofline": {"bound": "hbm", "kernel": f"adaln_bwd on {p.name} (row pass + finish)",
+        "roofline": {"bound": "hbm", "kernel": f"{bwd_name} on {p.name} (all of its launches)",
                      "achieved": round(bwd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(bwd_gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
     }

@@ -33,6 +33,7 @@ EXPORTED = (
     "adaln_bwd",
     "adaln_fwd_varlen",
     "adaln_bwd_varlen",
+    "adaln_bwd_twopass",
     "adaln_bwd_workspace_size",
     "adaln_status_str",
     "adaln_abi_version",
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, ctypes.c_size_t, _P,
                               _P, _P, _P]
     lib.adaln_bwd.restype = ctypes.c_int
+    lib.adaln_bwd_twopass.argtypes = lib.adaln_bwd.argtypes
+    lib.adaln_bwd_twopass.restype = ctypes.c_int
     lib.adaln_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P,
                                      ctypes.c_size_t, _P, _P, _P, _P]
     lib.adaln_bwd_varlen.restype = ctypes.c_int
@@ -197,8 +200,19 @@ def _workspace(B, R, D, dtype, dev, workspace):
 
 def adaln_bwd(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, dshift=None, stream=None):
     """Backward of a dense batch.  Returns (dx [B, N, D], dscale [B, D], dshift [B, D])."""
+    return _bwd_dense("adaln_bwd", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
+
+
+def adaln_bwd_twopass(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, dshift=None,
+                      stream=None):
+    """The same backward with the column reduction as a separate D-tile pass
+    that reads dy and x again (for comparison with the fused adaln_bwd)."""
+    return _bwd_dense("adaln_bwd_twopass", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
+
+
+def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream):
     if x.dim() != 3 or dy.shape != x.shape:
-        raise ValueError("adaln_bwd expects dy and x of shape [B, N, D]")
+        raise ValueError(f"{fn} expects dy and x of shape [B, N, D]")
     B, N, D = x.shape
     dx = torch.empty_like(x) if dx is None else dx
     dscale = torch.empty((B, D), dtype=x.dtype, device=x.device) if dscale is None else dscale
@@ -209,10 +223,10 @@ def adaln_bwd(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, ds
     lib = load_library()
     with torch.cuda.device(dev):
         workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace)
-        st = lib.adaln_bwd(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
-                           _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream), _ptr(dx),
-                           _ptr(dscale), _ptr(dshift))
-    _raise("adaln_bwd", st)
+        st = getattr(lib, fn)(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
+                              _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream), _ptr(dx),
+                              _ptr(dscale), _ptr(dshift))
+    _raise(fn, st)
     return dx, dscale, dshift
 
 

@@ -128,7 +128,7 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
                           const float* rstd, const int64_t* offsets, int64_t B, int64_t N,
                           int64_t R, int64_t D, adaln_dtype_t dtype, void* workspace,
                           size_t workspace_bytes, hipStream_t stream, void* dx, void* dscale,
-                          void* dshift) {
+                          void* dshift, bool twopass = false) {
   Sizes s;
   adaln_status_t st = check_shape(B, R, D, dtype, &s);
   if (st != ADALN_OK) return st;
@@ -156,13 +156,17 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
 
   const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true);
   const bool vec = vp.ok && aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(scale);
+  if (twopass && !vec) return ADALN_ERR_UNSUPPORTED_SHAPE;
   char* ws = static_cast<char*>(workspace);
   adaln::Tiling tl{wl.tile_rows, wl.tiles_max, wl.tiles_alloc,
                    offsets ? reinterpret_cast<int64_t*>(ws + wl.tile_start_off) : nullptr, 1};
   float* partial = reinterpret_cast<float*>(ws + wl.partial_off);
   const adaln::RowMap rm{B, R, N, offsets};
-  const hipError_t e = adaln::launch_bwd(dtype, dy, x, scale, mean, rstd, rm, D, vec, vp, tl,
-                                         partial, stream, dx, dscale, dshift);
+  const hipError_t e =
+      twopass ? adaln::launch_bwd_twopass(dtype, dy, x, scale, mean, rstd, rm, D, vp, tl, partial,
+                                          stream, dx, dscale, dshift)
+              : adaln::launch_bwd(dtype, dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial,
+                                  stream, dx, dscale, dshift);
   return e == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
@@ -219,6 +223,19 @@ ADALN_EXPORT adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, cons
   if (!offsets_dev) return ADALN_ERR_INVALID_ARG;
   return bwd_common(dy, x, scale, mean, rstd, offsets_dev, B, 0, total_rows, D, dtype, workspace,
                     workspace_bytes, stream, dx, dscale, dshift);
+}
+
+ADALN_EXPORT adaln_status_t adaln_bwd_twopass(const void* dy, const void* x, const void* scale,
+                                              const float* mean, const float* rstd, int64_t B,
+                                              int64_t N, int64_t D, adaln_dtype_t dtype,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, void* dx, void* dscale,
+                                              void* dshift) {
+  if (N < 0 || B < 1) return ADALN_ERR_INVALID_ARG;
+  int64_t R;
+  if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
+  return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
+                    workspace_bytes, stream, dx, dscale, dshift, true);
 }
 
 ADALN_EXPORT const char* adaln_status_str(adaln_status_t status) {

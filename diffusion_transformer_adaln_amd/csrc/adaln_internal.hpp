@@ -56,6 +56,14 @@ hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scal
                       bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
                       hipStream_t stream, void* dx, void* dscale, void* dshift);
 
+// The two-pass backward: dx rows, then D-tile column partials that read dy
+// and x again, then the finish.  Vectorised plans only (vp.ok, 16-byte
+// aligned rows).
+hipError_t launch_bwd_twopass(int dtype, const void* dy, const void* x, const void* scale,
+                              const float* mean, const float* rstd, const RowMap& rm, int64_t D,
+                              const VecPlan& vp, const Tiling& tl, float* partial,
+                              hipStream_t stream, void* dx, void* dscale, void* dshift);
+
 // Rows per backward tile for R rows on a device with num_cu compute units.
 int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen);
 

@@ -403,7 +403,9 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // Grid: one workgroup per tile (a run of rows inside one sample).
 // LDS: 2 buffers x [slots][RIF][groups] x (sum g, sum g*xhat), then, when a
 // workgroup holds several slots, [2][D] floats for the slot combine.
-template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool PF = true, bool OPAQUE = false>
+// COLS = false compiles out the column partials: dx only (the first pass of
+// the two-pass backward).
+template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool COLS = true>
 __global__ void __launch_bounds__(NTMAX)
 bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
                const uint4* __restrict__ scale, const float* __restrict__ mean,
@@ -467,16 +469,8 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 
   const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
   int it = 0;
-  if (PF) load_rows(0, xv, gv, mu, rs);
   for (int64_t base = 0; base < count; base += rows_per_iter, ++it) {
-    // with PF the next iteration's loads are in flight while this one reduces
-    uint4 xn[RIF][VPT], gn[RIF][VPT];
-    float mun[RIF], rsn[RIF];
-    if (PF) {
-      if (base + rows_per_iter < count) load_rows(base + rows_per_iter, xn, gn, mun, rsn);
-    } else {
-      load_rows(base, xv, gv, mu, rs);
-    }
+    load_rows(base, xv, gv, mu, rs);
 
     float sg[RIF], sgx[RIF];
 #pragma unroll
@@ -515,18 +509,6 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       }
     }
 
-    if (OPAQUE) {
-      // Hide the packed rows from the optimiser here, so the output pass
-      // unpacks them again instead of keeping the first pass's fp32 copies
-      // alive across the reduction (fewer VGPRs, more waves per SIMD).
-#pragma unroll
-      for (int i = 0; i < RIF; ++i)
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-          asm volatile("" : "+v"(xv[i][j].x), "+v"(xv[i][j].y), "+v"(xv[i][j].z), "+v"(xv[i][j].w));
-          asm volatile("" : "+v"(gv[i][j].x), "+v"(gv[i][j].y), "+v"(gv[i][j].z), "+v"(gv[i][j].w));
-        }
-    }
 #pragma unroll
     for (int i = 0; i < RIF; ++i) {
       const int64_t m = base + static_cast<int64_t>(slot) * RIF + i;
@@ -544,21 +526,16 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
           const float xh = (fx[k] - mu[i]) * rs[i];
           const float g = mul_rounded(fg[k], sc1[j][k]);   // same rounding in both passes
           out[k] = rs[i] * ((g - a) - xh * c);
-          acc_h[j][k] += fg[k];
-          acc_s[j][k] += fg[k] * xh;
+          if (COLS) {
+            acc_h[j][k] += fg[k];
+            acc_s[j][k] += fg[k] * xh;
+          }
         }
         store_stream(dxr + j * lpr, E::pack(out));
       }
     }
-    if (PF) {
-#pragma unroll
-      for (int i = 0; i < RIF; ++i) {
-        mu[i] = mun[i]; rs[i] = rsn[i];
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) { xv[i][j] = xn[i][j]; gv[i][j] = gn[i][j]; }
-      }
-    }
   }
+  if (!COLS) return;
 
   // tile partials, chunk-major (see pidx)
   const int64_t TA = tl.tiles_alloc;
@@ -596,6 +573,97 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       const int q = i / d4, col = (i - q * d4) * 4;
       *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) =
           *reinterpret_cast<const float4*>(comb + q * D + col);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// two-pass backward, second pass: D-tile column partials
+// ---------------------------------------------------------------------------
+// The backward's gradient reduction as the AdaptiveLoad summary lays it out
+// (section 2.B, backward bullet): after a separate dx pass, a grid of
+// (n_tile, d_tile) workgroups reads dy and x again; each thread is pinned to
+// one 16-byte vector of columns and adds sum(dy) and sum(dy*xhat) down the
+// rows of its tile, so the 64 lanes of a wave read one contiguous 1 KiB span
+// of a row.  It writes the same chunk-major tile partials as the fused row
+// pass, which gets them without the second read of dy and x; the two paths
+// exist side by side to measure what the fusion saves.
+// Grid: (tiles, ceil(V/64)); 256 threads = 4 waves.  Wave w adds the tile's
+// rows w, w+4, w+8, ... in ascending order (DT_UNROLL rows' loads in flight),
+// then the four wave sums are added in wave order.
+constexpr int DT_WAVES = 4;
+constexpr int DT_UNROLL = 4;
+
+template <int DT>
+__global__ void __launch_bounds__(64 * DT_WAVES)
+dtile_cols_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
+                  const float* __restrict__ mean, const float* __restrict__ rstd, RowMap rm,
+                  Tiling tl, int V, float* __restrict__ partial) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::EPV;
+  __shared__ float red[DT_WAVES - 1][64][2 * EPV];
+  const int64_t t = blockIdx.x;
+  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
+  int64_t b, first, step, count;
+  tile_rows_of(rm, tl, t, b, first, step, count);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int v = blockIdx.y * 64 + lane;
+  const bool on = v < V;
+
+  float ah[EPV], as[EPV];
+#pragma unroll
+  for (int k = 0; k < EPV; ++k) { ah[k] = 0.f; as[k] = 0.f; }
+  auto add_row = [&](const uint4& xv, const uint4& gv, float mu, float rs) {
+    float fx[EPV], fg[EPV];
+    E::unpack(xv, fx);
+    E::unpack(gv, fg);
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) {
+      const float xh = (fx[k] - mu) * rs;
+      ah[k] += fg[k];
+      as[k] += fg[k] * xh;
+    }
+  };
+  if (on) {
+    int64_t m = w;
+    for (; m + (DT_UNROLL - 1) * DT_WAVES < count; m += DT_UNROLL * DT_WAVES) {
+      uint4 xv[DT_UNROLL], gv[DT_UNROLL];
+      float mu[DT_UNROLL], rs[DT_UNROLL];
+#pragma unroll
+      for (int u = 0; u < DT_UNROLL; ++u) {
+        const int64_t row = first + (m + u * DT_WAVES) * step;
+        mu[u] = mean[row];
+        rs[u] = rstd[row];
+        xv[u] = load_stream(x + row * V + v);
+        gv[u] = load_stream(dy + row * V + v);
+      }
+#pragma unroll
+      for (int u = 0; u < DT_UNROLL; ++u) add_row(xv[u], gv[u], mu[u], rs[u]);
+    }
+    for (; m < count; m += DT_WAVES) {
+      const int64_t row = first + m * step;
+      add_row(load_stream(x + row * V + v), load_stream(dy + row * V + v), mean[row], rstd[row]);
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) { red[w - 1][lane][k] = ah[k]; red[w - 1][lane][EPV + k] = as[k]; }
+  }
+  __syncthreads();
+  if (w == 0 && on) {
+#pragma unroll
+    for (int q = 0; q < DT_WAVES - 1; ++q)
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) { ah[k] += red[q][lane][k]; as[k] += red[q][lane][EPV + k]; }
+    const int64_t TA = tl.tiles_alloc;
+    const int col = v * EPV;
+#pragma unroll
+    for (int k = 0; k < EPV; k += 4) {
+      *reinterpret_cast<float4*>(partial + pidx(TA, t, 0, col + k)) =
+          make_float4(ah[k], ah[k + 1], ah[k + 2], ah[k + 3]);
+      *reinterpret_cast<float4*>(partial + pidx(TA, t, 1, col + k)) =
+          make_float4(as[k], as[k + 1], as[k + 2], as[k + 3]);
     }
   }
 }
@@ -1006,7 +1074,7 @@ static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* s
   return hipGetLastError();
 }
 
-template <int DT, int VPT>
+template <int DT, int VPT, bool COLS = true>
 static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scale,
                                  const float* mean, const float* rstd, const RowMap& rm,
                                  int64_t D, const VecPlan& vp, const Tiling& tl, float* partial,
@@ -1015,7 +1083,7 @@ static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scal
   constexpr int RIF = BWD_RIF;
   const int V = static_cast<int>(D / EPV);
   const size_t lds = vec_lds_bytes(vp, D, true);
-  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF, VEC_MAX_NT, false>), dim3(static_cast<unsigned>(tl.tiles_max)),
+  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF, VEC_MAX_NT, COLS>), dim3(static_cast<unsigned>(tl.tiles_max)),
                      dim3(vp.nt), lds, stream, static_cast<const uint4*>(dy),
                      static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
                      tl, V, static_cast<int>(D), vp.lpr, partial, static_cast<uint4*>(dx));
@@ -1049,6 +1117,11 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
 }
 
 template <int DT>
+static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
+                                const float* partial, hipStream_t stream, void* dscale,
+                                void* dshift);
+
+template <int DT>
 static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
                                const float* mean, const float* rstd, const RowMap& rm, int64_t D,
                                bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
@@ -1076,8 +1149,15 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
     }
     if (e != hipSuccess) return e;
   }
-  // finish: the narrow kernel for few samples whose tiles fit one workgroup,
-  // else one workgroup per (sample, 64 columns)
+  return finish_launch<DT>(rm, D, tl, partial, stream, dscale, dshift);
+}
+
+// finish: the narrow kernel for few samples whose tiles fit one workgroup,
+// else one workgroup per (sample, 64 columns)
+template <int DT>
+static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
+                                const float* partial, hipStream_t stream, void* dscale,
+                                void* dshift) {
   const int64_t max_tiles_per_sample = (rm.R + tl.tile_rows - 1) / tl.tile_rows;
   if (D % 4 == 0 && rm.B <= NARROW_MAX_SAMPLES && max_tiles_per_sample <= NARROW_MAX_TILES) {
     const int col_blocks = static_cast<int>((D + PCOLS - 1) / PCOLS);
@@ -1093,6 +1173,41 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
   return hipGetLastError();
 }
 
+// Two-pass backward (vectorised shapes only): dx rows, then D-tile column
+// partials over contiguous sequence chunks, then the same finish.
+template <int DT>
+static hipError_t bwd_twopass_dispatch(const void* dy, const void* x, const void* scale,
+                                       const float* mean, const float* rstd, const RowMap& rm,
+                                       int64_t D, const VecPlan& vp, const Tiling& tl,
+                                       float* partial, hipStream_t stream, void* dx,
+                                       void* dscale, void* dshift) {
+  hipError_t e = hipSuccess;
+  if (rm.offsets != nullptr) {
+    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
+                       tl.tile_rows, tl.tile_start);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (rm.R > 0 && tl.tiles_max > 0) {
+    switch (vp.vpt) {
+      case 1: e = bwd_vec_launch<DT, 1, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+      case 2: e = bwd_vec_launch<DT, 2, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+      case 3: e = bwd_vec_launch<DT, 3, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+      case 4: e = bwd_vec_launch<DT, 4, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int V = static_cast<int>(D / Elem<DT>::EPV);
+    Tiling chunks = tl;
+    chunks.interleave = 0;
+    hipLaunchKernelGGL((dtile_cols_kernel<DT>),
+                       dim3(static_cast<unsigned>(tl.tiles_max), static_cast<unsigned>((V + 63) / 64)),
+                       dim3(64 * DT_WAVES), 0, stream, static_cast<const uint4*>(dy),
+                       static_cast<const uint4*>(x), mean, rstd, rm, chunks, V, partial);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return finish_launch<DT>(rm, D, tl, partial, stream, dscale, dshift);
+}
+
 hipError_t launch_fwd(int dtype, const void* x, const void* shift, const void* scale, float eps,
                       const RowMap& rm, int64_t D, bool vec, const VecPlan& vp, int num_cu,
                       hipStream_t stream, void* y, float* mean, float* rstd) {
@@ -1100,6 +1215,15 @@ hipError_t launch_fwd(int dtype, const void* x, const void* shift, const void* s
   return dtype == BF16
              ? fwd_dispatch<BF16>(x, shift, scale, eps, rm, D, vec, vp, num_cu, stream, y, mean, rstd)
              : fwd_dispatch<F32>(x, shift, scale, eps, rm, D, vec, vp, num_cu, stream, y, mean, rstd);
+}
+
+hipError_t launch_bwd_twopass(int dtype, const void* dy, const void* x, const void* scale,
+                              const float* mean, const float* rstd, const RowMap& rm, int64_t D,
+                              const VecPlan& vp, const Tiling& tl, float* partial,
+                              hipStream_t stream, void* dx, void* dscale, void* dshift) {
+  return dtype == BF16
+             ? bwd_twopass_dispatch<BF16>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx, dscale, dshift)
+             : bwd_twopass_dispatch<F32>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx, dscale, dshift);
 }
 
 hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scale,

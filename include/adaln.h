@@ -174,6 +174,31 @@ adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 void* dx, void* dscale, void* dshift);
 
+/*
+ * adaln_bwd_twopass -- the same backward as adaln_bwd, computed the way the
+ * AdaptiveLoad summary lays out its gradient reduction (section 2.B, backward
+ * bullet, "Reducción Coalescida D-tile") without fusing it into the dx pass:
+ *   1. a row pass that writes dx only;
+ *   2. a (n_tile, d_tile) grid that reads dy and x again, each thread pinned
+ *      to 8 (bf16) or 4 (fp32) adjacent features of one 16-byte vector,
+ *      adding dy and dy * xhat down a contiguous chunk of the sample's rows;
+ *   3. the same deterministic finish as adaln_bwd.
+ * It moves 2*R*D more elements through HBM than adaln_bwd and exists to
+ * measure what the fusion saves.  Arguments, ownership, workspace (the size
+ * adaln_bwd_workspace_size reports) and errors as in adaln_bwd, plus:
+ * ADALN_ERR_UNSUPPORTED_SHAPE unless dy, x, dx and scale are 16-byte aligned
+ * and D fits the vectorised row layout (D*element size a multiple of 16 and
+ * the row's 16-byte vectors divisible into 16-lane groups).  dx is bitwise
+ * identical to adaln_bwd's; dscale and dshift add the same terms in another
+ * fixed order, so they agree with adaln_bwd's to rounding and are bitwise
+ * repeatable from run to run.  Three launches.
+ */
+adaln_status_t adaln_bwd_twopass(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd,
+                                 int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 void* dx, void* dscale, void* dshift);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* adaln_status_str(adaln_status_t status);
 

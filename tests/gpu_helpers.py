@@ -53,8 +53,9 @@ def to_host64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(pd, eps=None, dense=None):
-    """Forward + backward of one problem on the GPU.  Returns device tensors."""
+def run_gpu(pd, eps=None, dense=None, twopass=False):
+    """Forward + backward of one problem on the GPU.  Returns device tensors.
+    twopass: dense batches only, backward through adaln_bwd_twopass."""
     import diffusion_transformer_adaln_amd as adaln
 
     p = pd.problem
@@ -67,9 +68,11 @@ def run_gpu(pd, eps=None, dense=None):
     if dense:
         B, N, D = p.B, p.N, p.D
         y, mean, rstd = adaln.adaln_fwd(x.view(B, N, D), shift, scale, eps)
-        dx, dscale, dshift = adaln.adaln_bwd(dy.view(B, N, D), x.view(B, N, D), scale, mean, rstd)
+        bwd = adaln.adaln_bwd_twopass if twopass else adaln.adaln_bwd
+        dx, dscale, dshift = bwd(dy.view(B, N, D), x.view(B, N, D), scale, mean, rstd)
         y, dx, mean, rstd = y.view(-1, D), dx.view(-1, D), mean.view(-1), rstd.view(-1)
     else:
+        assert not twopass, "the two-pass backward takes dense batches"
         off = torch.from_numpy(pd.offsets).cuda()
         y, mean, rstd = adaln.adaln_fwd_varlen(x, shift, scale, off, eps)
         dx, dscale, dshift = adaln.adaln_bwd_varlen(dy, x, scale, mean, rstd, off)

@@ -104,6 +104,17 @@ def test_backward_validation_codes(lib):
     assert bwd(lib, ws=FAKE * 6 + 4) == 1               # workspace not 16-byte aligned
 
 
+def test_twopass_validation_codes(lib):
+    def tp(dy=FAKE, dt=1, B=1, ws=FAKE * 6, ds=FAKE * 8):
+        return lib.adaln_bwd_twopass(P(dy), P(FAKE * 2), P(FAKE * 3), P(FAKE * 4), P(FAKE * 5), B, 4, 8, dt,
+                                     P(ws), 1 << 20, None, P(FAKE * 7), P(ds), P(FAKE * 9))
+    assert tp(dt=3) == 2
+    assert tp(B=0) == 1
+    assert tp(dy=0) == 1
+    assert tp(ds=0) == 1
+    assert tp(ws=FAKE * 6 + 4) == 1
+
+
 def test_workspace_query_rejects_bad_sizes(lib):
     assert lib.adaln_bwd_workspace_size(0, 10, 8, 1) == 0
     assert lib.adaln_bwd_workspace_size(1, -1, 8, 1) == 0

@@ -189,6 +189,57 @@ def test_dense_and_packed_agree(dtype, D, N, B):
 
 
 # ---------------------------------------------------------------------------
+# the two-pass (unfused D-tile) backward
+# ---------------------------------------------------------------------------
+TWOPASS = [("bf16", 5120, [1000]), ("bf16", 1152, [300] * 3), ("bf16", 3072, [77, 77]),
+           ("f32", 128, [999]), ("f32", 4096, [70]), ("bf16", 128, [255]), ("bf16", 16384, [5]),
+           ("bf16", 3072, [1])]
+
+
+@pytest.mark.parametrize("dtype,D,lengths", TWOPASS,
+                         ids=[f"{d}-D{D}-{'x'.join(map(str, l))}" for d, D, l in TWOPASS])
+def test_twopass_backward(dtype, D, lengths):
+    """Oracle parity for the two-pass backward; its dx is the fused path's dx
+    bit for bit (same row kernel), its column sums add the same terms in
+    another fixed order."""
+    pd = _pd(dtype, D, lengths, seed=41 + D, dy_sigma=1.0 if dtype == "f32" else 1e-2)
+    say(f"[twopass] {dtype} D={D} lengths={lengths}")
+    a = run_gpu(pd, twopass=True)
+    check_all(pd, a)
+    b = run_gpu(pd)
+    for k in ("y", "mean", "rstd", "dx"):
+        assert bits(a[k]) == bits(b[k]), k
+    h = {k: hashlib.sha256(bits(a[k])).hexdigest() for k in ("dscale", "dshift")}
+    for _ in range(3):
+        c = run_gpu(pd, twopass=True)
+        assert {k: hashlib.sha256(bits(c[k])).hexdigest() for k in ("dscale", "dshift")} == h
+
+
+def test_twopass_full_size_video_sampled():
+    pd = workloads.make_config("video_bf16")[0]
+    say("[twopass-full] video_bf16")
+    out = run_gpu(pd, twopass=True)
+    res = check_rows(pd, out, sampled_rows(pd))
+    res.update(check_samples(pd, out, np.arange(pd.problem.B)))
+    say(f"  {res}")
+
+
+def test_twopass_rejects_unvectorised_shapes():
+    import diffusion_transformer_adaln_amd as adaln
+
+    say("[twopass] unsupported shapes")
+    # D = 100 bf16: rows are not whole 16-byte vectors; D = 64 bf16: 8 vectors,
+    # fewer than one 16-lane group; D = 127 fp32: odd
+    for D, dt in ((100, torch.bfloat16), (64, torch.bfloat16), (127, torch.float32)):
+        x = torch.randn(1, 8, D, device="cuda").to(dt)
+        sc = torch.zeros(1, D, device="cuda").to(dt)
+        y, mean, rstd = adaln.adaln_fwd(x, sc, sc, 1e-6)
+        with pytest.raises(adaln.AdaLNError) as e:
+            adaln.adaln_bwd_twopass(x, x.clone(), sc, mean, rstd)
+        assert e.value.status == 3
+
+
+# ---------------------------------------------------------------------------
 # error codes through the real library
 # ---------------------------------------------------------------------------
 def test_error_codes_on_device():

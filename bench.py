@@ -26,6 +26,12 @@ workload's rows on one host core.
 `--bwd twopass` runs the backward through adaln_bwd_twopass instead (dx
 pass, then a separate D-tile column pass that reads dy and x again): the
 same work with more traffic, to measure what the fusion saves.
+
+`--impl torch` runs the unfused chain an eager framework executes instead
+(LayerNorm without affine, multiply by 1 + scale, add shift; backward by
+autograd), on the same resident copies, for context.  Every line reports
+`activation_bytes`: what the forward keeps alive for the backward beyond
+the inputs (the fused path: mean and rstd, 8 bytes per row).
 """
 
 from __future__ import annotations
@@ -57,6 +63,9 @@ def parse():
     ap.add_argument("--bwd", choices=("fused", "twopass"), default="fused",
                     help="backward entry point: the fused adaln_bwd, or adaln_bwd_twopass (dx pass, then "
                          "a separate D-tile column pass that reads dy and x again; dense workloads only)")
+    ap.add_argument("--impl", choices=("hip", "torch"), default="hip",
+                    help="hip: this library's kernels; torch: the unfused eager-PyTorch chain (dense "
+                         "workloads only), for comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -74,6 +83,37 @@ def upload(pd):
 
     return {"x": dev(pd.x), "dy": dev(pd.dy), "shift": dev(pd.shift), "scale": dev(pd.scale),
             "offsets": torch.from_numpy(pd.offsets).cuda()}
+
+
+def eager_adaln(x, shift, scale, eps):
+    """The unfused chain an eager framework runs for AdaLN on [B, N, D]:
+    LayerNorm without affine, multiply by (1 + scale), add shift, the
+    modulation broadcast over N.  Each step is its own kernel, and autograd
+    keeps what each step's backward needs."""
+    import torch.nn.functional as F
+
+    ln = F.layer_norm(x, (x.shape[-1],), eps=eps)
+    return ln * (1 + scale[:, None, :]) + shift[:, None, :]
+
+
+def saved_activation_bytes(fn, *args):
+    """Run fn(*args) and count the bytes of the distinct storages autograd
+    saves for its backward, leaving out the storages of the arguments
+    themselves (the caller holds those anyway).  Returns (output, bytes)."""
+    import torch
+
+    inputs = {a.untyped_storage().data_ptr() for a in args if torch.is_tensor(a)}
+    seen = {}
+
+    def pack(t):
+        st = t.untyped_storage()
+        if st.data_ptr() not in inputs:
+            seen[st.data_ptr()] = st.nbytes()
+        return t
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
+        out = fn(*args)
+    return out, sum(seen.values())
 
 
 def cpu_baseline(pd, seconds):
@@ -192,6 +232,49 @@ class Runner:
             ev_bwd[1].record()
 
 
+class TorchRunner:
+    """The unfused eager-PyTorch chain (eager_adaln) on resident copies laid
+    out like Runner's (dense workloads only): the forward builds the autograd
+    graph of its copy (replacing the previous one), the backward takes
+    torch.autograd.grad of it with the copy's dy."""
+
+    def __init__(self, pd, torch):
+        self.pd, self.p, self.torch = pd, pd.problem, torch
+        p = self.p
+        if not p.dense:
+            raise SystemExit(f"--impl torch takes dense workloads; {p.name} is packed")
+        base = upload(pd)
+        S = 4
+        per_set = max(1, 4 * p.R * p.D * p.esize)
+        while (S // 2 - 1) * per_set < (1 << 30) and S < 64:
+            S += 2
+        self.S = S
+        base["shift"].requires_grad_(True)
+        base["scale"].requires_grad_(True)
+        self.sets = [{"x": base["x"].clone().view(p.B, p.N, p.D).requires_grad_(True),
+                      "dy": base["dy"].clone().view(p.B, p.N, p.D), "shift": base["shift"],
+                      "scale": base["scale"], "y": None} for _ in range(S)]
+
+    def fwd(self, s):
+        s["y"] = eager_adaln(s["x"], s["shift"], s["scale"], self.p.eps)
+
+    def bwd(self, s):
+        # the graph stays alive: a copy's backward may run again before its
+        # next forward (the step order only fixes which copy each call uses)
+        self.torch.autograd.grad(s["y"], (s["x"], s["scale"], s["shift"]), s["dy"], retain_graph=True)
+
+    def prime(self):
+        for s in self.sets:
+            self.fwd(s)
+
+    step = Runner.step
+
+    def activation_bytes(self):
+        s = self.sets[0]
+        _, n = saved_activation_bytes(eager_adaln, s["x"], s["shift"], s["scale"], self.p.eps)
+        return n
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -210,7 +293,14 @@ def main():
 
     torch.cuda.set_device(0)
     pds = workloads.make_config(args.config)
-    runners = [Runner(pd, adaln, torch, args.bwd) for pd in pds]
+    if args.impl == "torch":
+        runners = [TorchRunner(pd, torch) for pd in pds]
+        act = sum(r.activation_bytes() for r in runners)
+        act_note = "eager chain: storages autograd saves beyond x, shift, scale"
+    else:
+        runners = [Runner(pd, adaln, torch, args.bwd) for pd in pds]
+        act = sum(8 * r.p.R for r in runners)
+        act_note = "fused: mean and rstd (fp32, 8 bytes per row)"
     nbytes = {k: sum(workloads.algorithmic_bytes(r.p)[k] for r in runners) for k in ("fwd", "bwd", "total")}
     rows = sum(r.p.R for r in runners)
     main_r = max(runners, key=lambda r: r.p.R * r.p.D)     # the roofline reports its backward
@@ -258,8 +348,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    traffic = read_traffic(args.traffic_file, args.config) if args.bwd == "fused" else None
+    traffic = read_traffic(args.traffic_file, args.config) if (args.bwd, args.impl) == ("fused", "hip") else None
     bwd_name = "adaln_bwd" if args.bwd == "fused" else "adaln_bwd_twopass"
+    if args.impl == "torch":
+        bwd_name = "eager PyTorch autograd backward"
 
     out = {
         "metric": METRIC,
@@ -278,13 +370,14 @@ def main():
                        f"{r.p.name}: AdaLN fwd+bwd, B={r.p.B}, N={r.p.N if r.p.dense else 'ragged'}, "
                        f"D={r.p.D}, {r.p.dtype} I/O, fp32 statistics" for r in runners),
                    "name": args.config, "B": sum(r.p.B for r in runners), "rows": rows,
-                   "D": p.D, "bwd": bwd_name, "parallelism": "single GPU"},
+                   "D": p.D, "impl": args.impl, "bwd": bwd_name, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
         "fwd_gbs": round(fwd_gbs, 1),
         "algorithmic_bytes_per_step": nbytes["total"],
+        "activation_bytes": {"saved": act, "what": act_note},
         "roofline": {"bound": "hbm", "kernel": f"{bwd_name} on {p.name} (all of its launches)",
                      "achieved": round(bwd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(bwd_gbs / PEAK_HBM_GBS, 4), "traffic": traffic},

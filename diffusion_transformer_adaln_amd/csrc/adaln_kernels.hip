@@ -784,9 +784,11 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
 // Few samples, at most NARROW_MAX_TILES tiles each: one 256-thread workgroup
 // per (sample, 16-column chunk).  Thread (slice, lane) adds tiles slice,
 // slice + 64, ... (ascending, at most 8) for 4 adjacent columns; the 64 slice
-// sums are then added in a fixed two-level order (8 runs of 8 slices, then the
-// run sums).  320 workgroups on the video shape, every load issued up front
-// over one contiguous run of partials: about one memory round trip.
+// sums are then added in a fixed two-level order (run r adds slices r, r+8,
+// ..., r+56, then the 8 run sums are added in run order).  320 workgroups on
+// the video shape, every load issued up front over one contiguous run of
+// partials: about one memory round trip.  The LDS layouts keep every access
+// of a wave on distinct banks (rocprofv3 SQ_LDS_BANK_CONFLICT = 0).
 constexpr int NARROW_LANES = PCOLS / 4;                  // float4 lanes per chunk
 constexpr int NARROW_SLICES = 256 / NARROW_LANES;        // 64
 constexpr int NARROW_PER = 8;                            // tiles per slice
@@ -802,8 +804,8 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   constexpr int RUNS = NSLICE / 8;
   __shared__ float4 sl_h[NSLICE][LANES];    // per-slice sums (fp32: at most PER tiles each)
   __shared__ float4 sl_s[NSLICE][LANES];
-  __shared__ double run_h[RUNS][LANES][4];
-  __shared__ double run_s[RUNS][LANES][4];
+  __shared__ double run_h[4][RUNS][LANES];  // component-major: a wave's stores are contiguous
+  __shared__ double run_s[4][RUNS][LANES];
   const int64_t b = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
   const int lane = threadIdx.x % LANES;
@@ -840,13 +842,13 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   if (slice < RUNS) {
     double a[4] = {0.0, 0.0, 0.0, 0.0}, c[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 x = sl_h[slice * 8 + q][lane], y = sl_s[slice * 8 + q][lane];
+    for (int q = 0; q < NSLICE / RUNS; ++q) {
+      const float4 x = sl_h[slice + q * RUNS][lane], y = sl_s[slice + q * RUNS][lane];
       a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
       c[0] += y.x; c[1] += y.y; c[2] += y.z; c[3] += y.w;
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) { run_h[slice][lane][w] = a[w]; run_s[slice][lane][w] = c[w]; }
+    for (int w = 0; w < 4; ++w) { run_h[w][slice][lane] = a[w]; run_s[w][slice][lane] = c[w]; }
   }
   __syncthreads();
   if (slice == 0 && col_ok) {
@@ -854,7 +856,7 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
     for (int w = 0; w < 4; ++w) {
       double a = 0.0, c = 0.0;
 #pragma unroll
-      for (int q = 0; q < RUNS; ++q) { a += run_h[q][lane][w]; c += run_s[q][lane][w]; }
+      for (int q = 0; q < RUNS; ++q) { a += run_h[w][q][lane]; c += run_s[w][q][lane]; }
       E::store1(dshift, b * D + d + w, static_cast<float>(a));
       E::store1(dscale, b * D + d + w, static_cast<float>(c));
     }

@@ -131,9 +131,15 @@ CONFIGS = {
     "ragged_bf16": (
         Problem("ragged_bf16", "bf16", RAGGED_D, ragged_lengths(), False, dy_sigma=1e-2),
     ),
+    # the sequence length at which the AdaptiveLoad summary quotes its backward
+    # speed-up and activation saving (section 4, kernel and memory bullets)
+    "long64k_bf16": (
+        Problem("long64k_bf16", "bf16", 5120, (64000,), True, dy_sigma=1e-3),
+    ),
 }
 
-CONFIG_SEEDS = {"tiny_fp32": 1, "dit_bf16": 2, "mmdit_bf16": 3, "video_bf16": 4, "ragged_bf16": 5}
+CONFIG_SEEDS = {"tiny_fp32": 1, "dit_bf16": 2, "mmdit_bf16": 3, "video_bf16": 4, "ragged_bf16": 5,
+                "long64k_bf16": 6}
 
 
 # --------------------------------------------------------------------------

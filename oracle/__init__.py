@@ -12,3 +12,4 @@ from .adaln_ref import (  # noqa: F401
     row_stats,
     sample_of_rows,
 )
+from .sched_ref import cost_model, fit_cost_model, load_cv, plan_groups  # noqa: F401

@@ -27,6 +27,9 @@ workload's rows on one host core.
 pass, then a separate D-tile column pass that reads dy and x again): the
 same work with more traffic, to measure what the fusion saves.
 
+`--cost-sweep` does the shape benchmarking of the batch scheduler instead
+(see cost_sweep) and prints its own JSON line.
+
 `--impl torch` runs the unfused chain an eager framework executes instead
 (LayerNorm without affine, multiply by 1 + scale, add shift; backward by
 autograd), on the same resident copies, for context.  Every line reports
@@ -66,6 +69,9 @@ def parse():
     ap.add_argument("--impl", choices=("hip", "torch"), default="hip",
                     help="hip: this library's kernels; torch: the unfused eager-PyTorch chain (dense "
                          "workloads only), for comparison")
+    ap.add_argument("--cost-sweep", action="store_true",
+                    help="time a synthetic per-group step over (B, S), fit step = a + b*B*S^p with "
+                         "adaln_cost_fit and compare equal-token and dual-constraint grouping")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -275,6 +281,97 @@ class TorchRunner:
         return n
 
 
+SWEEP_D = 3072            # AdaLN width of the synthetic step
+SWEEP_HEAD = 64           # width of the attention-score product
+SWEEP_M_MEM = 1 << 18     # tokens per group (the memory budget)
+
+
+def cost_sweep(adaln, torch, np):
+    """Shape benchmarking on one GPU: the single-GPU synthetic form of the
+    cost-fitting system of the AdaptiveLoad summary (section 2.A).
+
+    The timed per-group step is this library's AdaLN forward + backward on
+    [B, S, SWEEP_D] bf16 plus an fp32 attention-score product
+    [B, S, 64] x [B, 64, S] (the O(S^2) term of a DiT block), on every (B, S)
+    of a grid with B*S <= SWEEP_M_MEM.  adaln_cost_fit fits
+    step = a + b*B*S^p; M_comp is then the compute of one sequence of the
+    corpus's longest length, S_max^p: no group may cost more than the one
+    step no batching can shorten.
+    A seeded mixed-length corpus is cut into groups twice with
+    adaln_sched_plan, by equal tokens (M_comp unbounded) and by the dual
+    constraint, and each group's step is timed: the coefficient of variation
+    of those times is the load imbalance if each group went to its own GPU."""
+    import json as _json
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    cache = {}
+
+    def step_ms(B, S, reps=5):
+        key = (int(B), int(S))
+        if key in cache:
+            return cache[key]
+        g = torch.Generator(device="cuda").manual_seed(1234)
+        x = torch.randn(B, S, SWEEP_D, device="cuda", generator=g).to(torch.bfloat16)
+        dy = (1e-2 * torch.randn(B, S, SWEEP_D, device="cuda", generator=g)).to(torch.bfloat16)
+        mod = (0.1 * torch.randn(2, B, SWEEP_D, device="cuda", generator=g)).to(torch.bfloat16)
+        q = torch.randn(B, S, SWEEP_HEAD, device="cuda", generator=g)
+        kt = torch.randn(B, SWEEP_HEAD, S, device="cuda", generator=g)        # contiguous, not a view
+        ws = torch.empty(adaln.adaln_bwd_workspace_size(B, B * S, SWEEP_D, torch.bfloat16), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            y, mean, rstd = adaln.adaln_fwd(x, mod[0], mod[1], 1e-6)
+            torch.bmm(q, kt)
+            adaln.adaln_bwd(dy, x, mod[1], mean, rstd, workspace=ws)
+
+        for _ in range(2):
+            run()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        cache[key] = a.elapsed_time(b) / reps
+        del x, dy, q, kt, ws
+        torch.cuda.empty_cache()
+        return cache[key]
+
+    shapes = [(B, S) for S in (256, 512, 1024, 2048, 4096, 8192, 16384, 32760) for B in (1, 2, 4, 8)
+              if B * S <= SWEEP_M_MEM]
+    Bv = np.array([b for b, _ in shapes], dtype=np.float64)
+    Sv = np.array([s for _, s in shapes], dtype=np.float64)
+    tv = np.array([step_ms(b, s) for b, s in shapes])
+    a, b, p, rss = adaln.adaln_cost_fit(Bv, Sv, tv, 0.5, 3.0)
+    r_tok = float(np.corrcoef(tv, Bv * Sv)[0, 1])
+    r_sq = float(np.corrcoef(tv, Bv * Sv ** 2)[0, 1])
+    pred = lambda B, S: a + b * B * S ** p
+
+    rng = np.random.default_rng(7)
+    lengths = rng.choice([256, 1024, 4096, 16384, 32760], size=1024, p=[0.5, 0.2, 0.15, 0.1, 0.05])
+    m_comp = int(np.ceil(float(lengths.max()) ** p))
+    policies = {}
+    for name, mc in (("equal_tokens", np.iinfo(np.int64).max), ("dual_constraint", m_comp)):
+        group_of, n_groups = adaln.adaln_sched_plan(lengths, SWEEP_M_MEM, mc, p)
+        sizes = np.bincount(group_of, minlength=n_groups)
+        glen = np.zeros(n_groups, dtype=np.int64)
+        glen[group_of] = lengths
+        times = np.array([step_ms(int(n), int(S)) for n, S in zip(sizes, glen)])
+        model = np.array([pred(int(n), int(S)) for n, S in zip(sizes, glen)])
+        policies[name] = {"groups": int(n_groups), "cv_measured": round(adaln.adaln_load_cv(times), 4),
+                          "cv_model": round(adaln.adaln_load_cv(model), 4),
+                          "max_over_mean": round(float(times.max() / times.mean()), 3),
+                          "batch_by_length": {int(S): int(sizes[glen == S].max()) for S in np.unique(glen)}}
+    out = {"cost_sweep": {
+        "step": f"AdaLN fwd+bwd [B,S,{SWEEP_D}] bf16 + fp32 scores [B,S,{SWEEP_HEAD}]x[B,{SWEEP_HEAD},S]",
+        "shapes": len(shapes), "fit_ms": {"a": round(a, 5), "b": b, "p": round(p, 4), "rss": rss},
+        "corr_time_tokens": round(r_tok, 3), "corr_time_tokens_S2": round(r_sq, 3),
+        "m_mem": SWEEP_M_MEM, "m_comp": m_comp, "corpus": "1024 samples, lengths 256/1024/4096/16384/32760 "
+        "with probabilities 0.5/0.2/0.15/0.1/0.05 (seed 7)", "policies": policies,
+        "timings_ms": {f"{b}x{s}": round(t, 4) for (b, s), t in zip(shapes, tv)}}}
+    print(_json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -292,6 +389,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
+    if args.cost_sweep:
+        cost_sweep(adaln, torch, np)
+        return
     pds = workloads.make_config(args.config)
     if args.impl == "torch":
         runners = [TorchRunner(pd, torch) for pd in pds]
@@ -404,12 +504,17 @@ def read_traffic(path, config):
         return None
 
 
+# The sources the operator's kernels and launch configuration come from (the
+# host-only scheduler, csrc/adaln_sched.cpp, does not change them).
+OPERATOR_SOURCES = ("adaln_api.cpp", "adaln_internal.hpp", "adaln_kernels.hip")
+
+
 def kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "diffusion_transformer_adaln_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in OPERATOR_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -2,7 +2,8 @@
 
 The operator runs in hand-written HIP kernels behind the C ABI declared in
 include/adaln.h; this package holds those sources (csrc/), the build step and
-a ctypes binding whose functions carry the C entry points' names.
+a ctypes binding whose functions carry the C entry points' names.  The same
+library carries the host-side batch scheduler of include/adaln_sched.h.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -12,8 +13,12 @@ from ._lib import (  # noqa: F401
     adaln_bwd_twopass,
     adaln_bwd_varlen,
     adaln_bwd_workspace_size,
+    adaln_cost_fit,
     adaln_fwd,
     adaln_fwd_varlen,
+    adaln_load_cv,
+    adaln_sched_batch_size,
+    adaln_sched_plan,
     adaln_status_str,
     load_library,
 )

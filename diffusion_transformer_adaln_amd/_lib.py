@@ -37,6 +37,10 @@ EXPORTED = (
     "adaln_bwd_workspace_size",
     "adaln_status_str",
     "adaln_abi_version",
+    "adaln_sched_batch_size",
+    "adaln_sched_plan",
+    "adaln_cost_fit",
+    "adaln_load_cv",
 )
 
 
@@ -72,6 +76,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_bwd.restype = ctypes.c_int
     lib.adaln_bwd_twopass.argtypes = lib.adaln_bwd.argtypes
     lib.adaln_bwd_twopass.restype = ctypes.c_int
+    lib.adaln_sched_batch_size.argtypes = [_I64, _I64, _I64, ctypes.c_double]
+    lib.adaln_sched_batch_size.restype = _I64
+    lib.adaln_sched_plan.argtypes = [_P, _I64, _I64, _I64, ctypes.c_double, _P, _P]
+    lib.adaln_sched_plan.restype = ctypes.c_int
+    _D = ctypes.POINTER(ctypes.c_double)
+    lib.adaln_cost_fit.argtypes = [_P, _P, _P, _I64, ctypes.c_double, ctypes.c_double, _D, _D, _D, _D]
+    lib.adaln_cost_fit.restype = ctypes.c_int
+    lib.adaln_load_cv.argtypes = [_P, _I64]
+    lib.adaln_load_cv.restype = ctypes.c_double
     lib.adaln_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P,
                                      ctypes.c_size_t, _P, _P, _P, _P]
     lib.adaln_bwd_varlen.restype = ctypes.c_int
@@ -251,3 +264,56 @@ def adaln_bwd_varlen(dy, x, scale, mean, rstd, offsets, workspace=None, dx=None,
                                   _ptr(dx), _ptr(dscale), _ptr(dshift))
     _raise("adaln_bwd_varlen", st)
     return dx, dscale, dshift
+
+
+# ---------------------------------------------------------------------------
+# host-side scheduling (include/adaln_sched.h); numpy arrays in, no device use
+# ---------------------------------------------------------------------------
+def _host(a, dtype):
+    import numpy as np
+
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def adaln_sched_batch_size(S: int, m_mem: int, m_comp: int, p: float) -> int:
+    """B_shape(S) = max(1, min(m_mem // S, floor(m_comp / S**p))); raises on bad arguments."""
+    v = load_library().adaln_sched_batch_size(int(S), int(m_mem), int(m_comp), float(p))
+    if v < 0:
+        raise AdaLNError("adaln_sched_batch_size", 1)
+    return int(v)
+
+
+def adaln_sched_plan(lengths, m_mem: int, m_comp: int, p: float):
+    """Group index of every sample (int64 numpy array) and the group count."""
+    import numpy as np
+
+    lengths = _host(lengths, np.int64)
+    group_of = np.empty(lengths.size, dtype=np.int64)
+    n_groups = ctypes.c_int64(0)
+    st = load_library().adaln_sched_plan(lengths.ctypes.data if lengths.size else None, lengths.size, int(m_mem),
+                                         int(m_comp), float(p), group_of.ctypes.data if lengths.size else None,
+                                         ctypes.addressof(n_groups))
+    _raise("adaln_sched_plan", st)
+    return group_of, int(n_groups.value)
+
+
+def adaln_cost_fit(B, S, t, p_lo: float = 0.5, p_hi: float = 4.0):
+    """Least-squares fit of t = a + b*B*S**p; returns (a, b, p, rss)."""
+    import numpy as np
+
+    B, S, t = _host(B, np.float64), _host(S, np.float64), _host(t, np.float64)
+    if not (B.size == S.size == t.size):
+        raise ValueError("B, S and t must have the same length")
+    out = [ctypes.c_double(0.0) for _ in range(4)]
+    st = load_library().adaln_cost_fit(B.ctypes.data, S.ctypes.data, t.ctypes.data, B.size, float(p_lo),
+                                       float(p_hi), *[ctypes.byref(o) for o in out])
+    _raise("adaln_cost_fit", st)
+    return tuple(o.value for o in out)
+
+
+def adaln_load_cv(loads) -> float:
+    """Coefficient of variation (population std / mean) of per-worker loads."""
+    import numpy as np
+
+    x = _host(loads, np.float64)
+    return float(load_library().adaln_load_cv(x.ctypes.data if x.size else None, x.size))

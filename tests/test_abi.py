@@ -1,5 +1,5 @@
-"""The C-ABI library loads, exports every entry point include/adaln.h
-declares, and rejects bad arguments before touching a device (no kernels
+"""The C-ABI library loads, exports every entry point include/adaln.h and
+include/adaln_sched.h declare, and rejects bad arguments before touching a device (no kernels
 are launched here, and no HIP call is reached on these paths)."""
 
 import ctypes
@@ -13,13 +13,15 @@ import diffusion_transformer_adaln_amd as adaln
 from diffusion_transformer_adaln_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "adaln.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("adaln.h", "adaln_sched.h")]
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(adaln_[a-z_]+)\s*\(", src)))
+    names = set()
+    for path in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(adaln_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")

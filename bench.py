@@ -16,10 +16,13 @@ Infinity Cache cannot serve it and the figures are HBM figures.
 Output: one JSON line.  `value` is the whole-job throughput in GB/s of
 algorithmic bytes (the minimal traffic of the method, see
 workloads.algorithmic_bytes) over the wall-clock time of the K timed steps,
-bracketed by device synchronisation.  `roofline` covers the backward call,
-the dominant one: algorithmic bytes per call / mean call duration from HIP
-events recorded on the launch stream inside the timed region (around every
-fifth step's calls: each event adds a few microseconds of queue bubble).
+bracketed by device synchronisation; nothing else runs on the stream in that
+region (`gpu_ms_per_step` is the same region timed by two events on the
+launch stream).  `roofline` covers the backward call, the dominant one:
+algorithmic bytes per call / mean call duration from HIP events recorded on
+the launch stream in a second run of K steps right after the timed one
+(around every fifth step's calls; each timing event stalls the queue for
+several microseconds, which is why none sits inside the timed region).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
 
@@ -412,23 +415,35 @@ def main():
             r.step(k)
     torch.cuda.synchronize()
 
-    # Each recorded event costs a few microseconds of queue bubble, so event
-    # pairs bracket the calls of every SAMPLE-th step only: the forward on one
-    # sampled step, the backward on the next.
+    # Timed region: K steps and nothing else on the stream.  A timing event
+    # stalls the queue for several microseconds, so only two bracket the
+    # region (a GPU-side check of the host clock).
     K = args.steps
-    SAMPLE = 5
-    ev_f = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for k in range(0, K, SAMPLE)}
-    ev_b = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for k in range(SAMPLE // 2, K, SAMPLE)}
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    region = (ev(), ev())
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record()
     for k in range(K):
+        for r in runners:
+            r.step(k)
+    region[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms_per_step = region[0].elapsed_time(region[1]) / K
+
+    # Sampling region, right after on the same resident copies and step
+    # order: event pairs bracket the main workload's calls on every SAMPLE-th
+    # step (the forward on one sampled step, the backward on the next) and
+    # give per-call durations on the launch stream for the roofline.
+    SAMPLE = 5
+    ev_f = {k: (ev(), ev()) for k in range(K, 2 * K, SAMPLE)}
+    ev_b = {k: (ev(), ev()) for k in range(K + SAMPLE // 2, 2 * K, SAMPLE)}
+    for k in range(K, 2 * K):
         for r in runners:
             timed = r is main_r
             r.step(k, ev_f.get(k) if timed else None, ev_b.get(k) if timed else None)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     fwd_ms = np.array([a.elapsed_time(b) for a, b in ev_f.values()])
     bwd_ms = np.array([a.elapsed_time(b) for a, b in ev_b.values()])
@@ -461,6 +476,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

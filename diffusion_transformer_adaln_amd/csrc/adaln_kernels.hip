@@ -402,7 +402,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // ---------------------------------------------------------------------------
 // Grid: one workgroup per tile (a run of rows inside one sample).
 // LDS: 2 buffers x [slots][RIF][groups] x (sum g, sum g*xhat), then, when a
-// workgroup holds several slots, [2][D] floats for the slot combine.
+// workgroup holds several slots, [slots][D] floats for the slot combine.
 // COLS = false compiles out the column partials: dx only (the first pass of
 // the two-pass backward).
 template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool COLS = true>
@@ -552,27 +552,34 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       }
     }
   } else {
-    float* comb = reinterpret_cast<float*>(lds_f2 + 2 * buf_stride);   // [2][D]
-    __syncthreads();
-    for (int sl = 0; sl < nslots; ++sl) {
-      if (slot == sl) {
+    // Several slots: for each quantity, every slot stores its column sums to
+    // LDS ([slots][D]), then each thread adds a column over the slots in slot
+    // order and writes the tile partial.  Two barriers per quantity, however
+    // many slots.
+    float* comb = reinterpret_cast<float*>(lds_f2 + 2 * buf_stride);
+    const int d4 = D / 4;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-          const int col = (j * lpr + lane) * EPV;
+    for (int q = 0; q < 2; ++q) {
+      __syncthreads();                 // the reduction buffers / previous quantity are done
 #pragma unroll
-          for (int k = 0; k < EPV; ++k) {
-            if (sl == 0) { comb[col + k] = acc_h[j][k]; comb[D + col + k] = acc_s[j][k]; }
-            else { comb[col + k] += acc_h[j][k]; comb[D + col + k] += acc_s[j][k]; }
-          }
+      for (int j = 0; j < VPT; ++j) {
+        const int col = (j * lpr + lane) * EPV;
+#pragma unroll
+        for (int k = 0; k < EPV; k += 4) {
+          const float* a = q == 0 ? acc_h[j] : acc_s[j];
+          *reinterpret_cast<float4*>(comb + slot * D + col + k) = make_float4(a[k], a[k + 1], a[k + 2], a[k + 3]);
         }
       }
       __syncthreads();
-    }
-    const int d4 = D / 4;
-    for (int i = tid; i < 2 * d4; i += blockDim.x) {
-      const int q = i / d4, col = (i - q * d4) * 4;
-      *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) =
-          *reinterpret_cast<const float4*>(comb + q * D + col);
+      for (int i = tid; i < d4; i += blockDim.x) {
+        const int col = i * 4;
+        float4 v = *reinterpret_cast<const float4*>(comb + col);
+        for (int sl = 1; sl < nslots; ++sl) {
+          const float4 w = *reinterpret_cast<const float4*>(comb + sl * D + col);
+          v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) = v;
+      }
     }
   }
 }
@@ -955,14 +962,14 @@ varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile
 // plans and launchers
 // ---------------------------------------------------------------------------
 // Dynamic LDS of a vectorised launch: double-buffered per-row reduction
-// partials, plus the [2][D] slot-combine buffer of a multi-slot backward.
+// partials, plus the [slots][D] slot-combine buffer of a multi-slot backward.
 static size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
   const int nslots = p.nt / p.lpr;
   const int unit = (p.lpr % 64 == 0) ? 64 : (p.lpr == 32 ? 32 : 16);
   const int groups = p.lpr / unit;
   const int rif = backward ? BWD_RIF : FWD_RIF;
   size_t b = groups > 1 || backward ? 2 * static_cast<size_t>(nslots) * rif * groups * sizeof(float2) : 0;
-  if (backward && nslots > 1) b += 2 * static_cast<size_t>(D) * sizeof(float);
+  if (backward && nslots > 1) b += static_cast<size_t>(nslots) * D * sizeof(float);
   return b;
 }
 

@@ -268,3 +268,60 @@ def test_single_hip_runtime_mapped():
     adaln.load_library()
     libs = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
     assert len(libs) == 1, libs
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dense", [True, False])
+def test_graph_capture_replays_match_eager(dense):
+    """The entry points launch kernels only (no allocation, memset or
+    synchronisation), so a caller can capture them in a HIP graph.  Every
+    replay, with eager work and synchronisations in between, must give the
+    eager call's bits."""
+    import diffusion_transformer_adaln_amd as adaln
+
+    pd = _pd("bf16", 3072, [300] * 3 if dense else [300, 129, 64], seed=51, dense=dense)
+    p = pd.problem
+    say(f"[graph] dense={dense}")
+    x, dy = to_dev(pd.x, "bf16"), to_dev(pd.dy, "bf16")
+    sh, sc = to_dev(pd.shift, "bf16"), to_dev(pd.scale, "bf16")
+    off = torch.from_numpy(pd.offsets).cuda()
+    ws = torch.empty(adaln.adaln_bwd_workspace_size(p.B, p.R, p.D, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    mean = torch.empty(p.R, device="cuda")
+    rstd = torch.empty(p.R, device="cuda")
+    ds = torch.empty(p.B, p.D, dtype=torch.bfloat16, device="cuda")
+    dh = torch.empty_like(ds)
+
+    def call():
+        if dense:
+            v = lambda t: t.view(p.B, p.N, p.D)
+            adaln.adaln_fwd(v(x), sh, sc, p.eps, y=v(y), mean=mean.view(p.B, p.N), rstd=rstd.view(p.B, p.N))
+            adaln.adaln_bwd(v(dy), v(x), sc, mean.view(p.B, p.N), rstd.view(p.B, p.N), workspace=ws, dx=v(dx),
+                            dscale=ds, dshift=dh)
+        else:
+            adaln.adaln_fwd_varlen(x, sh, sc, off, p.eps, y=y, mean=mean, rstd=rstd)
+            adaln.adaln_bwd_varlen(dy, x, sc, mean, rstd, off, workspace=ws, dx=dx, dscale=ds, dshift=dh)
+
+    outs = lambda: {k: bits(t) for k, t in (("y", y), ("mean", mean), ("rstd", rstd), ("dx", dx),
+                                            ("dscale", ds), ("dshift", dh))}
+    call()
+    torch.cuda.synchronize()
+    ref = outs()
+    check_all(pd, {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dscale": ds, "dshift": dh})
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call()                          # warm-up on the capture stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for rep in range(4):
+        for t in (y, dx, mean, rstd, ds, dh, ws):
+            t.zero_()                   # eager work between replays; the graph must rewrite it all
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert outs() == ref, f"replay {rep} differs from the eager call"

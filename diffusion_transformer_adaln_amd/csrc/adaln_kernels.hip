@@ -553,9 +553,11 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
     }
   } else {
     // Several slots: for each quantity, every slot stores its column sums to
-    // LDS ([slots][D]), then each thread adds a column over the slots in slot
-    // order and writes the tile partial.  Two barriers per quantity, however
-    // many slots.
+    // LDS, then each thread adds a 4-column group over the slots in slot order
+    // and writes the tile partial.  Two barriers per quantity, however many
+    // slots.  A slot's D sums are stored as EPV/4 planes of V float4s (plane
+    // h holds columns 4h..4h+3 of every 16-byte vector), so the lanes of a
+    // wave store and load consecutive float4s: no LDS bank conflicts.
     float* comb = reinterpret_cast<float*>(lds_f2 + 2 * buf_stride);
     const int d4 = D / 4;
 #pragma unroll
@@ -563,21 +565,22 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       __syncthreads();                 // the reduction buffers / previous quantity are done
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
-        const int col = (j * lpr + lane) * EPV;
+        const int v = j * lpr + lane;
+        const float* a = q == 0 ? acc_h[j] : acc_s[j];
 #pragma unroll
-        for (int k = 0; k < EPV; k += 4) {
-          const float* a = q == 0 ? acc_h[j] : acc_s[j];
-          *reinterpret_cast<float4*>(comb + slot * D + col + k) = make_float4(a[k], a[k + 1], a[k + 2], a[k + 3]);
-        }
+        for (int h = 0; h < EPV / 4; ++h)
+          *reinterpret_cast<float4*>(comb + slot * D + (h * V + v) * 4) =
+              make_float4(a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]);
       }
       __syncthreads();
       for (int i = tid; i < d4; i += blockDim.x) {
-        const int col = i * 4;
-        float4 v = *reinterpret_cast<const float4*>(comb + col);
+        float4 v = *reinterpret_cast<const float4*>(comb + i * 4);
         for (int sl = 1; sl < nslots; ++sl) {
-          const float4 w = *reinterpret_cast<const float4*>(comb + sl * D + col);
+          const float4 w = *reinterpret_cast<const float4*>(comb + sl * D + i * 4);
           v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
         }
+        const int h = i / V;
+        const int col = (i - h * V) * EPV + h * 4;
         *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) = v;
       }
     }

@@ -84,6 +84,10 @@ SHAPES = [
     ("bf16", 1024, [100]), ("bf16", 2048, [64, 64]), ("bf16", 4096, [97]),
     ("bf16", 8192, [41]), ("bf16", 12288, [9]), ("bf16", 16384, [12]), ("bf16", 20000, [6]),
     ("bf16", 32768, [4]), ("f32", 65536, [3]), ("bf16", 65536, [3]),
+    # several rows per wave (16 or 32 lanes per row) with sample boundaries
+    # inside a wave's rows, so lanes of one wave use different modulation rows
+    ("bf16", 1152, [3, 5, 2, 7]), ("bf16", 1152, [13, 13]), ("f32", 128, [3, 1, 6]),
+    ("f32", 128, [5, 5, 5]), ("bf16", 256, [1, 0, 2, 9]),
 ]
 
 

@@ -7,11 +7,14 @@ kernel: forward, backward row pass, backward finish) over one resident batch
 of seeded synthetic bf16 inputs.  The default workload is the video-DiT
 AdaLN at one device's sequence share: B=1, N=18900, D=5120.
 
-Four copies of the inputs and outputs stay resident in HBM.  Step k runs the
-forward on copy k % 4 and the backward on copy (k + 2) % 4, the way a
-layer's backward runs long after its forward in training: no kernel reads
-data another kernel touched within the last ~1 GB of traffic, so the 256 MB
-Infinity Cache cannot serve it and the figures are HBM figures.
+S copies of the inputs and outputs stay resident in HBM (S >= 4, enough that
+about 1 GB of other traffic separates two touches of one copy; six for the
+video workload).  Step k runs the forward on copy k % S and the backward on
+copy (k + S/2) % S, the way a layer's backward runs long after its forward in
+training: no kernel reads data another kernel touched within the last ~1 GB
+of traffic, so the 256 MB Infinity Cache cannot serve it and the figures are
+HBM figures.  The warm-up runs at least 100 ms by default (the chip needs
+~20 ms under load to settle) unless --warmup fixes its step count.
 
 Output: one JSON line.  `value` is the whole-job throughput in GB/s of
 algorithmic bytes (the minimal traffic of the method, see
@@ -20,9 +23,10 @@ bracketed by device synchronisation; nothing else runs on the stream in that
 region (`gpu_ms_per_step` is the same region timed by two events on the
 launch stream).  `roofline` covers the backward call, the dominant one:
 algorithmic bytes per call / mean call duration from HIP events recorded on
-the launch stream in a second run of K steps right after the timed one
-(around every fifth step's calls; each timing event stalls the queue for
-several microseconds, which is why none sits inside the timed region).
+the launch stream right after the timed region, one event pair around each
+block of ten back-to-back calls (each timing event stalls the queue for a
+few microseconds, which is why none sits inside the timed region and why a
+pair does not bracket a single call).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
 
@@ -60,7 +64,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as take at least --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="minimum warm-up time when --warmup is not given")
     ap.add_argument("--config", default="video_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -227,18 +234,9 @@ class Runner:
         for s in self.sets:                 # every copy gets its statistics
             self.fwd(s)
 
-    def step(self, k, ev_fwd=None, ev_bwd=None):
-        sf, sb = self.sets[k % self.S], self.sets[(k + self.S // 2) % self.S]
-        if ev_fwd:
-            ev_fwd[0].record()
-        self.fwd(sf)
-        if ev_fwd:
-            ev_fwd[1].record()
-        if ev_bwd:
-            ev_bwd[0].record()
-        self.bwd(sb)
-        if ev_bwd:
-            ev_bwd[1].record()
+    def step(self, k):
+        self.fwd(self.sets[k % self.S])
+        self.bwd(self.sets[(k + self.S // 2) % self.S])
 
 
 class TorchRunner:
@@ -410,9 +408,25 @@ def main():
 
     for r in runners:
         r.prime()
-    for k in range(args.warmup):
-        for r in runners:
-            r.step(k)
+    # Warm-up.  Under sustained load the chip takes ~20 ms to settle: the
+    # video step runs 179-190 us for its first ~20 ms, then 172 us (measured in
+    # 10-step batches on MI355X), so by default the warm-up lasts at least
+    # --warmup-ms, in synchronised batches of 10 steps so that the host clock
+    # follows the GPU.  An explicit --warmup W runs exactly W steps.
+    warmup = 0
+    if args.warmup is not None:
+        for k in range(args.warmup):
+            for r in runners:
+                r.step(k)
+        warmup = args.warmup
+    else:
+        t_w = time.perf_counter()
+        while warmup < 20 or time.perf_counter() - t_w < args.warmup_ms * 1e-3:
+            for _ in range(10):
+                for r in runners:
+                    r.step(warmup)
+                warmup += 1
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # Timed region: K steps and nothing else on the stream.  A timing event
@@ -432,21 +446,29 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms_per_step = region[0].elapsed_time(region[1]) / K
 
-    # Sampling region, right after on the same resident copies and step
-    # order: event pairs bracket the main workload's calls on every SAMPLE-th
-    # step (the forward on one sampled step, the backward on the next) and
-    # give per-call durations on the launch stream for the roofline.
-    SAMPLE = 5
-    ev_f = {k: (ev(), ev()) for k in range(K, 2 * K, SAMPLE)}
-    ev_b = {k: (ev(), ev()) for k in range(K + SAMPLE // 2, 2 * K, SAMPLE)}
-    for k in range(K, 2 * K):
-        for r in runners:
-            timed = r is main_r
-            r.step(k, ev_f.get(k) if timed else None, ev_b.get(k) if timed else None)
-    torch.cuda.synchronize()
+    # Per-call durations for the roofline, right after, on the same resident
+    # copies and on the launch stream: blocks of BLOCK back-to-back calls of
+    # the main workload's backward (then forward), the copies rotating, one
+    # event pair per block.  A timing event between two kernels adds its own
+    # dispatch bubble (2-3 us here), so a pair around a single call reads
+    # high; over a block of ten the bubble is spread thin, and the figure still
+    # includes every launch gap of the calls themselves.
+    BLOCK = 10
 
-    fwd_ms = np.array([a.elapsed_time(b) for a, b in ev_f.values()])
-    bwd_ms = np.array([a.elapsed_time(b) for a, b in ev_b.values()])
+    def per_call_ms(call):
+        pairs = []
+        for b in range(max(1, K // BLOCK)):
+            e0, e1 = ev(), ev()
+            e0.record()
+            for i in range(BLOCK):
+                call(main_r.sets[(b * BLOCK + i) % main_r.S])
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in pairs]) / BLOCK
+
+    bwd_ms = per_call_ms(main_r.bwd)
+    fwd_ms = per_call_ms(main_r.fwd)
     ms_per_step = wall * 1e3 / K
     gbs = nbytes["total"] / (ms_per_step * 1e-3) / 1e9
     rows_per_s = rows / (ms_per_step * 1e-3)
@@ -474,7 +496,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "higher_is_better": True,

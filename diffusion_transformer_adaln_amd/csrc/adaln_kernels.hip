@@ -1260,7 +1260,10 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
       const int64_t cap = static_cast<int64_t>(num_cu) * (WAVE_NT / 64);
       const int64_t per = (units + cap - 1) / cap;
       if (per <= WAVE_MAX_UNITS) {
-        const int64_t active = (units + per - 1) / per;
+        // A batch of at most two units per wave runs one unit per wave on up to
+        // eight waves per CU instead (8192 x 1152 bf16: 9.6 against 11.1 us):
+        // with so little work per wave the prefetch has nothing to overlap.
+        const int64_t active = per <= 2 ? units : (units + per - 1) / per;
         return fwd_wave_launch<DT>(x, shift, scale, eps, rm, D, lpr, active, stream, y, mean, rstd);
       }
     }

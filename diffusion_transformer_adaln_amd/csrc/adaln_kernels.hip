@@ -410,8 +410,8 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // alternate (unrolled by two) so no register copy waits on the prefetch.
 // Measured on MI355X: a plain copy of a 18900 x 5120 bf16 tensor runs best
 // with ~16-20 KB of loads in flight per CU (6.2-6.4 TB/s) and slower with
-// more; this kernel takes the video-shape forward from 72-74 to 69-70 us, the
-// launch ramp of the many-workgroup kernel being what it removes.
+// more, which is what this grid is shaped by; in a warm fwd+bwd step it ties
+// the slot kernel on the video shape and is ~1% faster on D = 3072.
 constexpr int WAVE_NT = 256;            // four waves per workgroup, one workgroup per CU
 constexpr int WAVE_MAX_VPT = 10;
 constexpr int WAVE_MAX_UNITS = 32;      // beyond this many row units per wave the slot kernel wins
@@ -1211,16 +1211,17 @@ static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scal
   return hipGetLastError();
 }
 
-// Wave-per-row plan for the persistent forward: the widest of 64, 32, 16
-// lanes per row that splits the row into at most WAVE_MAX_VPT vectors per
-// lane.  Returns the lanes per row, or 0 if no such split exists.
+// Lanes per row for the persistent forward: a whole wave when the row splits
+// into at most WAVE_MAX_VPT vectors per lane, else 0 (the slot kernel).  The
+// kernel also runs rows of 16 or 32 lanes, several per wave, but measured in
+// a warm fwd+bwd step those are faster on the slot kernel (DiT, D = 1152:
+// 31.5 against 32.0 us per step), while 64-lane rows gain (MMDiT, D = 3072:
+// 83.4 against 84.4 us) or tie (video, D = 5120: 170.8 against 171.0 us).
 static int wave_lpr(int dtype, int64_t D) {
   const int epv = dtype == BF16 ? 8 : 4;
   if (D <= 0 || D % epv != 0) return 0;
   const int64_t V = D / epv;
-  for (int lpr : {64, 32, 16})
-    if (V % lpr == 0 && V / lpr <= WAVE_MAX_VPT) return lpr;
-  return 0;
+  return (V % 64 == 0 && V / 64 <= WAVE_MAX_VPT) ? 64 : 0;
 }
 
 template <int DT>
@@ -1260,10 +1261,7 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
       const int64_t cap = static_cast<int64_t>(num_cu) * (WAVE_NT / 64);
       const int64_t per = (units + cap - 1) / cap;
       if (per <= WAVE_MAX_UNITS) {
-        // A batch of at most two units per wave runs one unit per wave on up to
-        // eight waves per CU instead (8192 x 1152 bf16: 9.6 against 11.1 us):
-        // with so little work per wave the prefetch has nothing to overlap.
-        const int64_t active = per <= 2 ? units : (units + per - 1) / per;
+        const int64_t active = (units + per - 1) / per;
         return fwd_wave_launch<DT>(x, shift, scale, eps, rm, D, lpr, active, stream, y, mean, rstd);
       }
     }

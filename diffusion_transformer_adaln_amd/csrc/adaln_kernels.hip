@@ -398,69 +398,64 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 }
 
 // ---------------------------------------------------------------------------
-// persistent forward for rows that fit in one wave
+// persistent forward, one wave per row
 // ---------------------------------------------------------------------------
-// A row takes LPR = 16, 32 or 64 lanes (64/LPR rows per wave), so its
-// statistics need no LDS and no barrier.  A fixed grid of `active` waves
-// (about four per CU, one workgroup per CU) walks the rows grid-stride: wave g
-// takes row units g, g + active, ..., where a unit is the wave's 64/LPR
-// consecutive rows, so every wave gets the same number of units give or take
-// one and the chip sweeps memory in a narrow window.  Each wave loads its next
-// row while it reduces and writes the current one; the two row buffers
-// alternate (unrolled by two) so no register copy waits on the prefetch.
-// Measured on MI355X: a plain copy of a 18900 x 5120 bf16 tensor runs best
-// with ~16-20 KB of loads in flight per CU (6.2-6.4 TB/s) and slower with
-// more, which is what this grid is shaped by; in a warm fwd+bwd step it ties
-// the slot kernel on the video shape and is ~1% faster on D = 3072.
-constexpr int WAVE_NT = 256;            // four waves per workgroup, one workgroup per CU
+// For rows of 64 x VPT 16-byte vectors: a row is one wave (lane l holds
+// vectors l, l + 64, ...), so its statistics need no LDS and no barrier.  A
+// fixed grid of `active` waves (four per workgroup, about one workgroup per
+// CU) walks the rows grid-stride: wave g takes rows g, g + active, ..., so
+// every wave gets the same number of rows give or take one and the chip
+// sweeps memory in a narrow window.  Each wave loads its next row while it
+// reduces and writes the current one; the two row buffers alternate
+// (unrolled by two) so no register copy waits on the prefetch.  Measured on
+// MI355X: a plain copy of a 18900 x 5120 bf16 tensor runs best with ~16-20 KB
+// of loads in flight per CU (6.2-6.4 TB/s) and slower with more, which is what
+// this grid is shaped by; in a warm fwd+bwd step it ties the slot kernel on
+// the video shape and is ~1% faster on D = 3072.
+constexpr int WAVE_NT = 256;            // four waves per workgroup
 constexpr int WAVE_MAX_VPT = 10;
-constexpr int WAVE_MAX_UNITS = 32;      // beyond this many row units per wave the slot kernel wins
+constexpr int WAVE_MAX_ROWS = 32;       // beyond this many rows per wave the slot kernel wins
 
 template <int DT, int VPT>
 __global__ void __launch_bounds__(WAVE_NT)
 fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
-                const uint4* __restrict__ scale, float eps, RowMap rm, int V, int D, int lpr,
-                int64_t active, uint4* __restrict__ y, float* __restrict__ mean,
-                float* __restrict__ rstd) {
+                const uint4* __restrict__ scale, float eps, RowMap rm, int D, int64_t active,
+                uint4* __restrict__ y, float* __restrict__ mean, float* __restrict__ rstd) {
   using E = Elem<DT>;
   constexpr int EPV = E::EPV;
+  constexpr int V = 64 * VPT;               // vectors per row
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (gw >= active) return;
-  const int lane64 = threadIdx.x & 63;
-  const int rpw = 64 / lpr;
-  const int sub = lane64 / lpr;
-  const int lane = lane64 - sub * lpr;
-  const int64_t stride = active * rpw;      // rows between a wave's consecutive units
+  const int lane = threadIdx.x & 63;
   const int64_t last = rm.R - 1;
   const float inv_d = 1.0f / static_cast<float>(D);
   constexpr float n_lane = static_cast<float>(VPT * EPV);
 
   uint4 sc[VPT], sh[VPT];                   // the current sample's modulation, as stored
   int64_t cur_lo = 0, cur_hi = 0;
-  // Rows past the end load the last row instead (always in bounds) and are
-  // then ignored: the loads are unconditional so the compiler's wait counts
-  // stay exact and the prefetch stays in flight.
+  // Past the last row the prefetch loads the last row again (always in
+  // bounds) and nothing uses it: the loads are unconditional so the
+  // compiler's wait counts stay exact and the prefetch stays in flight.
   auto load_row = [&](uint4 (&dst)[VPT], int64_t r) {
     const uint4* xr = x + (r < last ? r : last) * V + lane;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) dst[j] = load_stream(xr + j * lpr);
+    for (int j = 0; j < VPT; ++j) dst[j] = load_stream(xr + j * 64);
   };
   auto step = [&](uint4 (&cur)[VPT], uint4 (&nxt)[VPT], int64_t r) {
-    const bool valid = r < rm.R;
-    if (valid && (r >= cur_hi || r < cur_lo)) {
+    if (r >= cur_hi || r < cur_lo) {
       const int64_t b = sample_of_row(rm, r);
       cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
       cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
-        sc[j] = scale[b * V + lane + j * lpr];
-        sh[j] = shift[b * V + lane + j * lpr];
+        sc[j] = scale[b * V + lane + j * 64];
+        sh[j] = shift[b * V + lane + j * 64];
       }
       // vmcnt(0): the reload settles inside its branch, so the common path
       // reaches the join with only the row loads and stores outstanding
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    load_row(nxt, r + stride);
+    load_row(nxt, r + active);
     __builtin_amdgcn_sched_barrier(0);      // keep the prefetch ahead of the reduction
 
     float f[VPT][EPV];
@@ -478,9 +473,8 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
       for (int k = 0; k < EPV; ++k) { const float d = f[j][k] - ml; sq += d * d; }
     float m = ml, s = sq;
-    chan_reduce_unit(m, s, n_lane, lpr);
+    chan_reduce_unit(m, s, n_lane, 64);
     const float rs = 1.0f / sqrtf(s * inv_d + eps);
-    if (!valid) return;
     if (lane == 0) { mean[r] = m; rstd[r] = rs; }
     uint4* yr = y + r * V + lane;
 #pragma unroll
@@ -492,17 +486,16 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
       // rstd = eps^-1/2, where x*rstd - mean*rstd would lose the digits)
 #pragma unroll
       for (int k = 0; k < EPV; ++k) o[k] = __builtin_fmaf((f[j][k] - m) * rs, a[k] + 1.0f, h[k]);
-      store_stream(yr + j * lpr, E::pack(o));
+      store_stream(yr + j * 64, E::pack(o));
     }
   };
 
-  int64_t row = gw * rpw + sub;
   uint4 xa[VPT], xb[VPT];
-  load_row(xa, row);
-  for (int64_t base = gw * rpw; base < rm.R; base += 2 * stride, row += 2 * stride) {
+  load_row(xa, gw);
+  for (int64_t row = gw; row < rm.R; row += 2 * active) {
     step(xa, xb, row);
-    if (base + stride >= rm.R) break;
-    step(xb, xa, row + stride);
+    if (row + active >= rm.R) break;
+    step(xb, xa, row + active);
   }
 }
 
@@ -1211,32 +1204,30 @@ static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scal
   return hipGetLastError();
 }
 
-// Lanes per row for the persistent forward: a whole wave when the row splits
-// into at most WAVE_MAX_VPT vectors per lane, else 0 (the slot kernel).  The
-// kernel also runs rows of 16 or 32 lanes, several per wave, but measured in
-// a warm fwd+bwd step those are faster on the slot kernel (DiT, D = 1152:
-// 31.5 against 32.0 us per step), while 64-lane rows gain (MMDiT, D = 3072:
-// 83.4 against 84.4 us) or tie (video, D = 5120: 170.8 against 171.0 us).
-static int wave_lpr(int dtype, int64_t D) {
+// Vectors per lane for the persistent forward: a row of 64 x VPT vectors with
+// VPT <= WAVE_MAX_VPT, else 0 (the slot kernel).  Measured in a warm fwd+bwd
+// step, the persistent kernel gains on such rows (MMDiT, D = 3072: 83.4
+// against 84.4 us per step) or ties (video, D = 5120: 170.8 against 171.0),
+// while rows of 16 or 32 lanes, several per wave, were faster on the slot
+// kernel (DiT, D = 1152: 31.5 against 32.0 us per step).
+static int wave_vpt(int dtype, int64_t D) {
   const int epv = dtype == BF16 ? 8 : 4;
   if (D <= 0 || D % epv != 0) return 0;
   const int64_t V = D / epv;
-  return (V % 64 == 0 && V / 64 <= WAVE_MAX_VPT) ? 64 : 0;
+  return (V % 64 == 0 && V / 64 <= WAVE_MAX_VPT) ? static_cast<int>(V / 64) : 0;
 }
 
 template <int DT>
 static hipError_t fwd_wave_launch(const void* x, const void* shift, const void* scale, float eps,
-                                  const RowMap& rm, int64_t D, int lpr, int64_t active,
+                                  const RowMap& rm, int64_t D, int vpt, int64_t active,
                                   hipStream_t stream, void* y, float* mean, float* rstd) {
-  const int V = static_cast<int>(D / Elem<DT>::EPV);
-  const int vpt = V / lpr;
   const int64_t grid = (active + WAVE_NT / 64 - 1) / (WAVE_NT / 64);
 #define ADALN_WAVE_CASE(N)                                                                          \
   case N:                                                                                          \
     hipLaunchKernelGGL((fwd_wave_kernel<DT, N>), dim3(static_cast<unsigned>(grid)), dim3(WAVE_NT), \
                        0, stream, static_cast<const uint4*>(x), static_cast<const uint4*>(shift),  \
-                       static_cast<const uint4*>(scale), eps, rm, V, static_cast<int>(D), lpr,     \
-                       active, static_cast<uint4*>(y), mean, rstd);                                \
+                       static_cast<const uint4*>(scale), eps, rm, static_cast<int>(D), active,     \
+                       static_cast<uint4*>(y), mean, rstd);                                        \
     break;
   switch (vpt) {
     ADALN_WAVE_CASE(1) ADALN_WAVE_CASE(2) ADALN_WAVE_CASE(3) ADALN_WAVE_CASE(4) ADALN_WAVE_CASE(5)
@@ -1253,16 +1244,15 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
                                int num_cu, hipStream_t stream, void* y, float* mean, float* rstd) {
   if (vec) {
     // The persistent wave kernel when each of ~4 waves per CU gets at most
-    // WAVE_MAX_UNITS row units; the active wave count is trimmed so the units
-    // divide as evenly as possible.
-    const int lpr = wave_lpr(DT, D);
-    if (lpr > 0) {
-      const int64_t units = (rm.R + (64 / lpr) - 1) / (64 / lpr);
+    // WAVE_MAX_ROWS rows; the active wave count is trimmed so the rows divide
+    // as evenly as possible.
+    const int wvpt = wave_vpt(DT, D);
+    if (wvpt > 0) {
       const int64_t cap = static_cast<int64_t>(num_cu) * (WAVE_NT / 64);
-      const int64_t per = (units + cap - 1) / cap;
-      if (per <= WAVE_MAX_UNITS) {
-        const int64_t active = (units + per - 1) / per;
-        return fwd_wave_launch<DT>(x, shift, scale, eps, rm, D, lpr, active, stream, y, mean, rstd);
+      const int64_t per = (rm.R + cap - 1) / cap;
+      if (per <= WAVE_MAX_ROWS) {
+        const int64_t active = (rm.R + per - 1) / per;
+        return fwd_wave_launch<DT>(x, shift, scale, eps, rm, D, wvpt, active, stream, y, mean, rstd);
       }
     }
     switch (vp.vpt) {

@@ -455,9 +455,6 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
       // reaches the join with only the row loads and stores outstanding
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
-    load_row(nxt, r + active);
-    __builtin_amdgcn_sched_barrier(0);      // keep the prefetch ahead of the reduction
-
     float f[VPT][EPV];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) E::unpack(cur[j], f[j]);
@@ -473,6 +470,13 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
       for (int k = 0; k < EPV; ++k) { const float d = f[j][k] - ml; sq += d * d; }
     float m = ml, s = sq;
+    // The next row's loads go out here, once this row's own pass over its
+    // registers is done, and stay in flight through the reduction and the
+    // output (measured: 67.1 us against 68.0 with them issued before the
+    // statistics, which keeps two rows per wave in flight for longer).
+    __builtin_amdgcn_sched_barrier(0);
+    load_row(nxt, r + active);
+    __builtin_amdgcn_sched_barrier(0);
     chan_reduce_unit(m, s, n_lane, 64);
     const float rs = 1.0f / sqrtf(s * inv_d + eps);
     if (lane == 0) { mean[r] = m; rstd[r] = rs; }
@@ -490,12 +494,17 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
     }
   };
 
+  // The first row is peeled off so that every entry into the loop finds the
+  // same memory operations outstanding (a prefetch into xb, then the stores):
+  // otherwise the compiler merges the entry path into the loop head and
+  // waits for everything there.
   uint4 xa[VPT], xb[VPT];
   load_row(xa, gw);
-  for (int64_t row = gw; row < rm.R; row += 2 * active) {
-    step(xa, xb, row);
+  step(xa, xb, gw);                         // gw < active <= R
+  for (int64_t row = gw + active; row < rm.R; row += 2 * active) {
+    step(xb, xa, row);
     if (row + active >= rm.R) break;
-    step(xb, xa, row + active);
+    step(xa, xb, row + active);
   }
 }
 

@@ -88,6 +88,10 @@ SHAPES = [
     # inside a wave's rows, so lanes of one wave use different modulation rows
     ("bf16", 1152, [3, 5, 2, 7]), ("bf16", 1152, [13, 13]), ("f32", 128, [3, 1, 6]),
     ("f32", 128, [5, 5, 5]), ("bf16", 256, [1, 0, 2, 9]),
+    # one-wave rows of every width the persistent forward instantiates
+    # (64 lanes x 1..10 vectors), with ragged and multi-sample batches
+    ("bf16", 512, [33, 2]), ("bf16", 1536, [40]), ("bf16", 2560, [50, 3]), ("bf16", 3584, [33]),
+    ("bf16", 4608, [7, 70]), ("f32", 1280, [40]), ("f32", 1792, [9, 9]), ("f32", 2560, [21]),
 ]
 
 

@@ -546,7 +546,7 @@ def read_traffic(path, config):
 
 # The sources the operator's kernels and launch configuration come from (the
 # host-only scheduler, csrc/adaln_sched.cpp, does not change them).
-OPERATOR_SOURCES = ("adaln_api.cpp", "adaln_internal.hpp", "adaln_kernels.hip")
+OPERATOR_SOURCES = ("adaln_api.cpp", "adaln_internal.hpp", "adaln_kernels.hip", "adaln_plan.cpp")
 
 
 def kernel_source_sha():

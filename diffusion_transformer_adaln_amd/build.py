@@ -3,6 +3,7 @@
     python -m diffusion_transformer_adaln_amd.build
 
 Compiles csrc/adaln_api.cpp (host: validation and dispatch),
+csrc/adaln_plan.cpp (host: row layouts, backward tiling, workspace layout),
 csrc/adaln_sched.cpp (host: batch scheduling and cost model) and
 csrc/adaln_kernels.hip (gfx950 kernels) with hipcc into one shared library
 next to this file.  Every call recompiles.
@@ -21,8 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libadaln.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = [os.path.join(CSRC, "adaln_api.cpp"), os.path.join(CSRC, "adaln_sched.cpp"),
-           os.path.join(CSRC, "adaln_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "adaln_api.cpp"), os.path.join(CSRC, "adaln_plan.cpp"),
+           os.path.join(CSRC, "adaln_sched.cpp"), os.path.join(CSRC, "adaln_kernels.hip")]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 HIPCC_FLAGS = [

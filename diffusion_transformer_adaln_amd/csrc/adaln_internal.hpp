@@ -1,5 +1,7 @@
-// Internal interface between the host dispatcher (adaln_api.cpp) and the
-// kernel launchers (adaln_kernels.hip).  Not part of the public ABI.
+// Internal interface between the host dispatcher (adaln_api.cpp), the host
+// planning code (adaln_plan.cpp: row layouts, backward tiling, workspace
+// layout) and the kernel launchers (adaln_kernels.hip).  Not part of the
+// public ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -42,8 +44,28 @@ struct VecPlan {
   int nt;
 };
 
+// Largest workgroup of the vectorised kernels: 8 waves, i.e. two per SIMD, so
+// the compiler may give each wave up to 256 VGPRs.
+constexpr int VEC_MAX_NT = 512;
+// Rows each slot handles per loop iteration.  Measured on MI355X, one row
+// per slot with more workgroups resident beats deeper per-slot batching or
+// register prefetch: both cost VGPRs, hence occupancy, which is what keeps
+// HBM requests in flight here.
+constexpr int FWD_RIF = 1;
+constexpr int BWD_RIF = 1;
+constexpr int FWD_MAX_VPT = 8;
+constexpr int BWD_MAX_VPT = 4;
+// Tile partial sums are stored chunk-major: for each 16-column chunk, the
+// tiles' 16-float rows of sum(dy) and sum(dy*xhat) follow each other, so the
+// finish reads each chunk's tiles as one contiguous run (on MI355X this cut the
+// finish from 10.0 to 6.4 us on the video shape against a tile-major layout).
+constexpr int PCOLS = 16;
+
 // Vector plan for the forward (backward = false) or backward kernels.
 VecPlan plan_vec(int dtype, int64_t D, bool backward);
+
+// Dynamic LDS bytes of a vectorised launch with plan p.
+size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward);
 
 // Launchers.  Each returns hipSuccess or the launch error.  They assume the
 // arguments were validated by the caller.

@@ -1,0 +1,105 @@
+// Host planning for the AdaLN kernels: the vectorised row layout, the
+// backward's tiling and the layout of its workspace.  Plain C++ (no device
+// code), shared by the dispatcher and the kernel launchers, and compiled on
+// its own by the host validation test.
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "adaln_internal.hpp"
+
+namespace adaln {
+
+// Dynamic LDS of a vectorised launch: double-buffered per-row reduction
+// partials, plus the [slots][D] slot-combine buffer of a multi-slot backward.
+size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
+  const int nslots = p.nt / p.lpr;
+  const int unit = (p.lpr % 64 == 0) ? 64 : (p.lpr == 32 ? 32 : 16);
+  const int groups = p.lpr / unit;
+  const int rif = backward ? BWD_RIF : FWD_RIF;
+  size_t b = groups > 1 || backward ? 2 * static_cast<size_t>(nslots) * rif * groups * 2 * sizeof(float) : 0;
+  if (backward && nslots > 1) b += static_cast<size_t>(nslots) * D * sizeof(float);
+  return b;
+}
+
+// Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,
+// LPR a multiple of 16.  Measured on MI355X (video shape, D = 5120 bf16):
+//   forward  about 40 elements per lane (two waves per row at D = 5120) with
+//            two rows per workgroup is fastest; one wave per row runs out of
+//            registers, and wide rows of 8-16 elements per lane spend their
+//            time in cross-wave reductions;
+//   backward 16 elements per lane (VPT = 2) keeps the per-column
+//            accumulators, the modulation row and the row data small enough
+//            for four waves per SIMD.
+// Ties prefer rows that cover whole waves (no partial-wave reductions).
+VecPlan plan_vec(int dtype, int64_t D, bool backward) {
+  VecPlan best{false, 0, 0, 0};
+  const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
+  const int epv = dtype == BF16 ? 8 : 4;
+  if (D <= 0 || D % epv != 0) return best;
+  const int64_t V = D / epv;
+  const int want = backward ? 16 : 40;           // elements per lane
+  int best_score = 1 << 30;
+  for (int vpt = 1; vpt <= max_vpt; ++vpt) {
+    if (V % vpt) continue;
+    const int64_t lpr = V / vpt;
+    if (lpr % 16 || lpr > VEC_MAX_NT) continue;
+    VecPlan p{true, vpt, static_cast<int>(lpr), 0};
+    // threads per workgroup: a multiple of both the row lanes and the wave,
+    // at least 128 (short rows share a workgroup)
+    int nt = p.lpr;
+    while (nt % 64) nt += p.lpr;
+    const int min_nt = 128;
+    while (nt < min_nt && nt * 2 <= VEC_MAX_NT) nt *= 2;
+    if (nt > VEC_MAX_NT) continue;
+    p.nt = nt;
+    if (vec_lds_bytes(p, D, backward) > 65536) continue;
+    const int el = vpt * epv;
+    const int score = (el > want ? el - want : want - el) + (lpr % 64 ? 16 : 0);
+    if (score < best_score) { best_score = score; best = p; }
+  }
+  return best;
+}
+
+// Backward tiles per compute unit for dense batches: a tile's column partials
+// cost 8*D bytes written and read again, so fewer, longer tiles are cheaper;
+// two per CU measured best on the video shape (one: 150 us, three: 159 us,
+// two: 107 us).
+constexpr int BWD_TILES_PER_CU = 2;
+// Packed batches mix short and long samples, so their tiles vary in length;
+// four tiles per CU lets the workgroup dispatcher even out the load (mixed
+// 256..32760-row samples at D = 3072: 952 us at two per CU, 907 at four, 927
+// at eight).
+constexpr int BWD_VARLEN_TILES_PER_CU = 4;
+int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen) {
+  const int64_t target =
+      static_cast<int64_t>(num_cu) * (varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU);
+  return R <= 0 ? 1 : (R + target - 1) / target;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
+                                     int64_t N_dense) {
+  WorkspaceLayout w{};
+  w.tile_rows = bwd_tile_rows(R, num_cu, varlen);
+  const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;   // tiles of any row split
+  w.tiles_alloc = bound;
+  w.tiles_max = varlen ? bound : B * ((N_dense + w.tile_rows - 1) / w.tile_rows);
+  w.tile_start_off = 0;
+  w.partial_off = align256(static_cast<size_t>(B + 1) * sizeof(int64_t));
+  const int64_t chunks = (D + PCOLS - 1) / PCOLS;
+  w.total = w.partial_off +
+            static_cast<size_t>(chunks) * static_cast<size_t>(bound) * 2 * PCOLS * sizeof(float);
+  return w;
+}
+
+// Enough for either entry point: the packed layout's tile bound covers any
+// row split, and the dense one is checked as well in case its tiles are finer.
+size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu) {
+  const size_t packed = bwd_workspace_layout(B, R, D, num_cu, true, 0).total;
+  const size_t dense = bwd_workspace_layout(B, R, D, num_cu, false, B > 0 ? R / B : 0).total;
+  return packed > dense ? packed : dense;
+}
+
+}  // namespace adaln

@@ -1,0 +1,249 @@
+// Host-only test of the C ABI's argument validation (include/adaln.h, "Errors"):
+// the real dispatcher (csrc/adaln_api.cpp) and planning code (csrc/adaln_plan.cpp)
+// linked against stub launchers that count launches and a stub device query
+// that reports one 256-CU device.  Built with the host compiler under
+// AddressSanitizer and UndefinedBehaviorSanitizer by tests/test_host_validation.py.
+//
+// Checks, for every entry point: each documented error code is returned for
+// its cause, a failing call launches nothing, a valid call launches exactly
+// once with the shape it was given, adaln_bwd_workspace_size() is enough for
+// both backward entry points, and each of them accepts exactly its own
+// workspace layout and rejects one byte less.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <limits>
+
+#include "adaln.h"
+#include "../../diffusion_transformer_adaln_amd/csrc/adaln_internal.hpp"
+
+// ---------------------------------------------------------------------------
+// stubs: one device with 256 compute units; launchers record their calls
+// ---------------------------------------------------------------------------
+static int g_launches = 0;
+static adaln::RowMap g_rm{};
+static int64_t g_D = 0;
+static adaln::Tiling g_tl{};
+
+hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t attr, int) {
+  if (attr != hipDeviceAttributeMultiprocessorCount) return hipErrorInvalidValue;
+  *v = 256;
+  return hipSuccess;
+}
+
+namespace adaln {
+hipError_t launch_fwd(int, const void*, const void*, const void*, float, const RowMap& rm, int64_t D,
+                      bool, const VecPlan&, int, hipStream_t, void*, float*, float*) {
+  ++g_launches; g_rm = rm; g_D = D;
+  return hipSuccess;
+}
+hipError_t launch_bwd(int, const void*, const void*, const void*, const float*, const float*,
+                      const RowMap& rm, int64_t D, bool, const VecPlan&, const Tiling& tl, float*,
+                      hipStream_t, void*, void*, void*) {
+  ++g_launches; g_rm = rm; g_D = D; g_tl = tl;
+  return hipSuccess;
+}
+hipError_t launch_bwd_twopass(int, const void*, const void*, const void*, const float*,
+                              const float*, const RowMap& rm, int64_t D, const VecPlan&,
+                              const Tiling& tl, float*, hipStream_t, void*, void*, void*) {
+  ++g_launches; g_rm = rm; g_D = D; g_tl = tl;
+  return hipSuccess;
+}
+}  // namespace adaln
+
+// ---------------------------------------------------------------------------
+// checks
+// ---------------------------------------------------------------------------
+static int g_failures = 0, g_checks = 0;
+
+#define EXPECT(cond, ...)                                          \
+  do {                                                             \
+    ++g_checks;                                                    \
+    if (!(cond)) {                                                 \
+      ++g_failures;                                                \
+      std::printf("FAIL %s:%d: ", __FILE__, __LINE__);             \
+      std::printf(__VA_ARGS__);                                    \
+      std::printf("\n");                                           \
+    }                                                              \
+  } while (0)
+
+// A call that must fail with `want` and launch nothing.
+#define REJECT(want, call)                                                                  \
+  do {                                                                                      \
+    const int before_ = g_launches;                                                         \
+    const adaln_status_t got_ = (call);                                                     \
+    EXPECT(got_ == (want), "%s: got %s, want %s", #call, adaln_status_str(got_),           \
+           adaln_status_str(want));                                                         \
+    EXPECT(g_launches == before_, "%s: launched on error", #call);                          \
+  } while (0)
+
+// A call that must succeed with exactly `n` launches.
+#define ACCEPT(n, call)                                                                     \
+  do {                                                                                      \
+    const int before_ = g_launches;                                                         \
+    const adaln_status_t got_ = (call);                                                     \
+    EXPECT(got_ == ADALN_OK, "%s: got %s", #call, adaln_status_str(got_));                 \
+    EXPECT(g_launches == before_ + (n), "%s: %d launches, want %d", #call,                  \
+           g_launches - before_, (n));                                                      \
+  } while (0)
+
+// Fake device addresses: validation never dereferences them.  Each buffer
+// gets its own 64 GiB region so nothing overlaps unless a test says so.
+static void* at(int region) { return reinterpret_cast<void*>(static_cast<uintptr_t>(region) << 36); }
+static float* fat(int region) { return static_cast<float*>(at(region)); }
+
+static void test_forward() {
+  const int64_t B = 2, N = 100, D = 1152;
+  void *x = at(1), *sh = at(2), *sc = at(3), *y = at(4);
+  float *m = fat(5), *r = fat(6);
+  const adaln_dtype_t bf = ADALN_BF16;
+
+  ACCEPT(1, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, y, m, r));
+  EXPECT(g_rm.B == B && g_rm.R == B * N && g_rm.N == N && g_rm.offsets == nullptr && g_D == D,
+         "forward launched with the wrong shape");
+  ACCEPT(0, adaln_fwd(x, sh, sc, 1e-6f, B, 0, D, bf, nullptr, y, m, r));   // empty batch
+  ACCEPT(0, adaln_fwd(nullptr, sh, sc, 1e-6f, B, 0, D, bf, nullptr, nullptr, nullptr, nullptr));
+  ACCEPT(1, adaln_fwd(x, sh, sc, 0.0f, B, N, D, ADALN_F32, nullptr, y, m, r));
+
+  REJECT(ADALN_ERR_UNSUPPORTED_DTYPE, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, (adaln_dtype_t)7, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, 0, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, B, -1, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, B, N, 0, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_UNSUPPORTED_SHAPE, adaln_fwd(x, sh, sc, 1e-6f, B, N, ADALN_MAX_D + 1, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_UNSUPPORTED_SHAPE, adaln_fwd(x, sh, sc, 1e-6f, INT64_MAX / 4, 8, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_UNSUPPORTED_SHAPE, adaln_fwd(x, sh, sc, 1e-6f, 1, INT64_MAX / 1024, 4096, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, -1e-6f, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, NAN, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, INFINITY, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(nullptr, sh, sc, 1e-6f, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, nullptr, sc, 1e-6f, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, nullptr, 1e-6f, B, N, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, nullptr, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, y, nullptr, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, y, m, nullptr));
+  // aliasing: y over x (in place), y over shift, mean over rstd, y ending one byte into x
+  REJECT(ADALN_ERR_ALIASING, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, x, m, r));
+  REJECT(ADALN_ERR_ALIASING, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, sh, m, r));
+  REJECT(ADALN_ERR_ALIASING, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, y, m, m + 1));
+  char* xb = static_cast<char*>(x);
+  const int64_t bytes = B * N * D * 2;
+  REJECT(ADALN_ERR_ALIASING, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, xb - bytes + 1, m, r));
+  ACCEPT(1, adaln_fwd(x, sh, sc, 1e-6f, B, N, D, bf, nullptr, xb - bytes, m, r));   // adjacent is fine
+}
+
+static void test_forward_varlen() {
+  const int64_t B = 3, R = 77, D = 3072;
+  void *x = at(1), *sh = at(2), *sc = at(3), *y = at(4);
+  float *m = fat(5), *r = fat(6);
+  const int64_t* off = static_cast<const int64_t*>(at(7));
+  const adaln_dtype_t bf = ADALN_BF16;
+  ACCEPT(1, adaln_fwd_varlen(x, sh, sc, 1e-6f, off, B, R, D, bf, nullptr, y, m, r));
+  EXPECT(g_rm.B == B && g_rm.R == R && g_rm.offsets == off && g_D == D, "varlen forward launched with the wrong shape");
+  ACCEPT(0, adaln_fwd_varlen(x, sh, sc, 1e-6f, off, B, 0, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd_varlen(x, sh, sc, 1e-6f, nullptr, B, R, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd_varlen(x, sh, sc, 1e-6f, off, 0, R, D, bf, nullptr, y, m, r));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_fwd_varlen(x, sh, sc, 1e-6f, off, B, -5, D, bf, nullptr, y, m, r));
+  // the offsets are an input: an output over them is aliasing
+  REJECT(ADALN_ERR_ALIASING, adaln_fwd_varlen(x, sh, sc, 1e-6f, off, B, R, D, bf, nullptr, y,
+                                              reinterpret_cast<float*>(const_cast<int64_t*>(off)), r));
+}
+
+static void test_backward() {
+  const int64_t B = 2, N = 4096, D = 3072;
+  void *dy = at(1), *x = at(2), *sc = at(3), *dx = at(4), *dsc = at(5), *dsh = at(6), *ws = at(9);
+  const float *m = fat(7), *r = fat(8);
+  const adaln_dtype_t bf = ADALN_BF16;
+  const size_t need = adaln_bwd_workspace_size(B, B * N, D, bf);
+  EXPECT(need > 0, "workspace size query returned 0 for a valid shape");
+
+  for (int pass = 0; pass < 2; ++pass) {
+    auto call = [&](void* dy_, void* x_, void* sc_, const float* m_, const float* r_, int64_t B_, int64_t N_,
+                    int64_t D_, adaln_dtype_t dt, void* ws_, size_t wsb, void* dx_, void* dsc_, void* dsh_) {
+      return pass == 0 ? adaln_bwd(dy_, x_, sc_, m_, r_, B_, N_, D_, dt, ws_, wsb, nullptr, dx_, dsc_, dsh_)
+                       : adaln_bwd_twopass(dy_, x_, sc_, m_, r_, B_, N_, D_, dt, ws_, wsb, nullptr, dx_, dsc_, dsh_);
+    };
+    ACCEPT(1, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dx, dsc, dsh));
+    EXPECT(g_rm.B == B && g_rm.R == B * N && g_rm.N == N && g_D == D && g_tl.tiles_max > 0 &&
+               g_tl.tiles_max <= g_tl.tiles_alloc && g_tl.tile_start == nullptr,
+           "backward launched with the wrong shape or tiling");
+    const size_t own = adaln::bwd_workspace_layout(B, B * N, D, 256, false, N).total;
+    EXPECT(own <= need, "dense layout larger than the size query");
+    ACCEPT(1, call(dy, x, sc, m, r, B, N, D, bf, ws, own, dx, dsc, dsh));
+    REJECT(ADALN_ERR_WORKSPACE_TOO_SMALL, call(dy, x, sc, m, r, B, N, D, bf, ws, own - 1, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, N, D, bf, nullptr, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, N, D, bf, static_cast<char*>(ws) + 8, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_UNSUPPORTED_DTYPE, call(dy, x, sc, m, r, B, N, D, (adaln_dtype_t)-1, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, 0, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, -1, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_UNSUPPORTED_SHAPE, call(dy, x, sc, m, r, B, N, ADALN_MAX_D * 2, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(nullptr, x, sc, m, r, B, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, nullptr, sc, m, r, B, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, nullptr, m, r, B, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, nullptr, r, B, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, nullptr, B, N, D, bf, ws, need, dx, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dsc, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dx, nullptr, dsh));
+    REJECT(ADALN_ERR_INVALID_ARG, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dx, dsc, nullptr));
+    // aliasing: dx over dy, dscale over dshift, dshift inside the workspace, workspace over x
+    REJECT(ADALN_ERR_ALIASING, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dy, dsc, dsh));
+    REJECT(ADALN_ERR_ALIASING, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dx, dsc, static_cast<char*>(dsc) + 2));
+    REJECT(ADALN_ERR_ALIASING, call(dy, x, sc, m, r, B, N, D, bf, ws, need, dx, dsc, static_cast<char*>(ws) + 2));
+    REJECT(ADALN_ERR_ALIASING, call(dy, x, sc, m, r, B, N, D, bf, x, need, dx, dsc, dsh));
+  }
+  // N == 0: the backward still runs (its finish writes zero dscale/dshift)
+  ACCEPT(1, adaln_bwd(nullptr, nullptr, sc, nullptr, nullptr, B, 0, D, bf, ws, adaln_bwd_workspace_size(B, 0, D, bf),
+                      nullptr, nullptr, dsc, dsh));
+  // workspace query: invalid sizes give 0
+  EXPECT(adaln_bwd_workspace_size(0, 10, D, bf) == 0, "B = 0 accepted by the size query");
+  EXPECT(adaln_bwd_workspace_size(B, -1, D, bf) == 0, "negative rows accepted by the size query");
+  EXPECT(adaln_bwd_workspace_size(B, 10, 0, bf) == 0, "D = 0 accepted by the size query");
+  EXPECT(adaln_bwd_workspace_size(B, 10, D, (adaln_dtype_t)9) == 0, "bad dtype accepted by the size query");
+}
+
+static void test_backward_varlen() {
+  // the size query covers the packed layout as well as the dense one
+  const adaln_dtype_t bf = ADALN_BF16;
+  void *dy = at(1), *x = at(2), *sc = at(3), *dx = at(4), *dsc = at(5), *dsh = at(6), *ws = at(9);
+  const float *m = fat(7), *r = fat(8);
+  const int64_t* off = static_cast<const int64_t*>(at(10));
+  const int64_t shapes[][3] = {{277, 229368, 3072}, {1, 18900, 5120}, {5, 3, 128}, {300, 300, 1152}, {2, 1, 8}};
+  for (const auto& s : shapes) {
+    const int64_t B = s[0], R = s[1], D = s[2];
+    const size_t need = adaln_bwd_workspace_size(B, R, D, bf);
+    ACCEPT(1, adaln_bwd_varlen(dy, x, sc, m, r, off, B, R, D, bf, ws, need, nullptr, dx, dsc, dsh));
+    EXPECT(g_rm.offsets == off && g_tl.tile_start != nullptr && g_tl.tiles_max <= g_tl.tiles_alloc,
+           "packed backward tiling inconsistent for B=%lld R=%lld", (long long)B, (long long)R);
+    const size_t own = adaln::bwd_workspace_layout(B, R, D, 256, true, 0).total;
+    EXPECT(own <= need, "packed layout larger than the size query");
+    REJECT(ADALN_ERR_WORKSPACE_TOO_SMALL,
+           adaln_bwd_varlen(dy, x, sc, m, r, off, B, R, D, bf, ws, own - 1, nullptr, dx, dsc, dsh));
+    if (R % B == 0) {
+      ACCEPT(1, adaln_bwd(dy, x, sc, m, r, B, R / B, D, bf, ws, need, nullptr, dx, dsc, dsh));
+    }
+  }
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_bwd_varlen(dy, x, sc, m, r, nullptr, 2, 10, 64, bf, ws, 1 << 20, nullptr, dx, dsc, dsh));
+}
+
+static void test_status_strings() {
+  for (int s = 0; s <= 6; ++s) EXPECT(adaln_status_str((adaln_status_t)s) != nullptr, "null status string");
+  EXPECT(adaln_status_str((adaln_status_t)42) != nullptr, "null string for an unknown code");
+  EXPECT(adaln_abi_version() == ADALN_ABI_VERSION, "ABI version mismatch");
+}
+
+int main() {
+  test_forward();
+  test_forward_varlen();
+  test_backward();
+  test_backward_varlen();
+  test_status_strings();
+  std::printf("%d checks, %d failures, %d launches\n", g_checks, g_failures, g_launches);
+  return g_failures == 0 ? 0 : 1;
+}

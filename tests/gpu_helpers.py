@@ -16,6 +16,14 @@ judged on that absolute scale.  Two stricter internal gates are applied as well:
 normwise error max|got-ref| / max|ref| of y and dx at most 1e-2 (bf16) or
 1e-5 (fp32), and fp32 statistics (mean, rstd) within 1e-5 relative to the
 row's scale.
+
+Rows far from zero mean (|mean| >> std): an fp32 row mean is itself rounded,
+by a few u*|mean|, and that error shifts every xhat of the row by the same
+amount, so a column sum of dy*xhat carries an extra absolute error up to
+C*u*sum_r |dy_rd|*|mean_r|*rstd_r whatever the implementation, as long as its
+statistics are fp32.  Checks of such inputs add that allowance (C = 4) to the
+dscale bound (mean_rounding=True); for the workloads' centred rows it is
+negligible and left out.
 """
 
 from __future__ import annotations
@@ -33,6 +41,8 @@ TOL = {
 }
 STAT_TOL = 1e-5
 REL_FLOOR = 1e-2
+MEAN_ULPS = 4.0
+U32 = 2.0 ** -24
 
 
 def say(msg):
@@ -126,8 +136,11 @@ def assert_norm(got, ref, tol, what):
     return e
 
 
-def assert_rel_floored(got, ref, tol, what):
-    """Per sample row: |got-ref| / max(|ref|, 1e-2 * rms(ref))."""
+def assert_rel_floored(got, ref, tol, what, extra=None):
+    """Per sample row: |got-ref| <= tol * max(|ref|, 1e-2 * rms(ref)) + extra.
+
+    Returns the worst ratio of error to bound scaled by tol (the plain relative
+    error when extra is None)."""
     worst = 0.0
     for i in range(ref.shape[0]):
         r = ref[i]
@@ -136,8 +149,10 @@ def assert_rel_floored(got, ref, tol, what):
             e = float(np.abs(got[i]).max()) if r.size else 0.0
             assert e == 0.0, f"{what}[{i}]: expected exact zeros, max |got| {e:.3e}"
             continue
-        rel = np.abs(got[i] - r) / np.maximum(np.abs(r), REL_FLOOR * rms)
-        worst = max(worst, float(rel.max()))
+        bound = tol * np.maximum(np.abs(r), REL_FLOOR * rms)
+        if extra is not None:
+            bound = bound + extra[i]
+        worst = max(worst, float((np.abs(got[i] - r) / bound).max()) * tol)
     assert worst <= tol, f"{what}: max relative error {worst:.3e} > {tol:.1e}"
     return worst
 
@@ -170,8 +185,11 @@ def check_rows(pd, out, rows, eps=None, strict=True):
     return res
 
 
-def check_samples(pd, out, samples, eps=None):
-    """dscale and dshift of the given samples (full column sums) against the oracle."""
+def check_samples(pd, out, samples, eps=None, mean_rounding=False):
+    """dscale and dshift of the given samples (full column sums) against the oracle.
+
+    mean_rounding: add the fp32-mean rounding allowance to the dscale bound
+    (inputs whose rows sit far from zero mean; see the module docstring)."""
     p = pd.problem
     eps = p.eps if eps is None else eps
     samples = np.asarray(samples, dtype=np.int64)
@@ -179,6 +197,7 @@ def check_samples(pd, out, samples, eps=None):
         return {}
     ds_ref = np.zeros((samples.size, p.D))
     dh_ref = np.zeros((samples.size, p.D))
+    allow = np.zeros((samples.size, p.D)) if mean_rounding else None
     scale_all = oracle.decode(pd.scale, p.dtype)
     for i, b in enumerate(samples):
         lo, hi = int(pd.offsets[b]), int(pd.offsets[b + 1])
@@ -188,20 +207,24 @@ def check_samples(pd, out, samples, eps=None):
         dy = oracle.decode(pd.dy[lo:hi], p.dtype)
         _, ds, dh = oracle.adaln_bwd(dy, x, scale_all[b:b + 1], eps, np.array([0, hi - lo]))
         ds_ref[i], dh_ref[i] = ds[0], dh[0]
+        if mean_rounding:
+            _, m, rs = oracle.adaln_fwd(x, np.zeros((1, p.D)), np.zeros((1, p.D)), eps,
+                                        np.array([0, hi - lo]))
+            allow[i] = MEAN_ULPS * U32 * (np.abs(m) * rs) @ np.abs(dy)
     idx = torch.from_numpy(samples).cuda()
     ds = to_host64(out["dscale"].index_select(0, idx))
     dh = to_host64(out["dshift"].index_select(0, idx))
     t = TOL[p.dtype]
     return {
-        "dscale_rel": assert_rel_floored(ds, ds_ref, t["rel"], "dscale"),
+        "dscale_rel": assert_rel_floored(ds, ds_ref, t["rel"], "dscale", allow),
         "dshift_rel": assert_rel_floored(dh, dh_ref, t["rel"], "dshift"),
     }
 
 
-def check_all(pd, out, eps=None, strict=True):
+def check_all(pd, out, eps=None, strict=True, mean_rounding=False):
     p = pd.problem
     r = check_rows(pd, out, np.arange(p.R), eps, strict)
-    r.update(check_samples(pd, out, np.arange(p.B), eps))
+    r.update(check_samples(pd, out, np.arange(p.B), eps, mean_rounding))
     return r
 
 

@@ -4,7 +4,8 @@ Small problems (several tiles plus a ragged tail) are checked in full;
 the full-size workloads are checked on sampled rows and on whole-sample
 column sums.  Edge cases: empty inputs and samples, one-row samples, odd and
 tiny D, misaligned pointers (general kernels), the largest supported D,
-constant rows, determinism and dense/packed equivalence.
+constant rows, rows far from zero mean, determinism and dense/packed
+equivalence.
 """
 
 import hashlib
@@ -163,6 +164,28 @@ def test_constant_rows(dtype, D):
         # rstd = eps^-1/2 makes |dx| large: outside the workloads' range, where
         # the bf16 format itself sets the error floor
         check_all(pd, run_gpu(pd, eps=eps), eps=eps, strict=False)
+
+
+# Per-row offsets far above the row's spread (|mean|/std up to ~200 in fp32):
+# the statistics must not cancel.  A one-pass E[x^2] - E[x]^2 variance in fp32
+# loses most of its digits here (xhat off by ~3e-2 in an fp32 emulation, 300x
+# the fp32 bound on y and dx); per-lane two-pass sums merged with Chan's update
+# stay near 1e-5.  The dscale bound adds the rounding of the fp32 row mean
+# itself (a few u*|mean| per row, common to the whole row), which no fp32
+# implementation avoids.  One case per forward kernel: the one-wave-per-row
+# kernel (D = 5120 bf16, D = 1280 fp32), the slot kernel (D = 4096 fp32,
+# D = 1152 bf16, packed), the general kernel (D = 100).
+OFFSET_CASES = [("f32", 1280, [40], 64.0), ("f32", 4096, [70], 64.0), ("f32", 100, [33, 9], 64.0),
+                ("bf16", 5120, [300], 32.0), ("bf16", 1152, [3, 50, 7], 32.0)]
+
+
+@pytest.mark.parametrize("dtype,D,lengths,sigma", OFFSET_CASES,
+                         ids=[f"{d}-D{D}-{'x'.join(map(str, l))}" for d, D, l, _ in OFFSET_CASES])
+def test_large_row_offsets(dtype, D, lengths, sigma):
+    pd = _pd(dtype, D, lengths, seed=17 + D, dy_sigma=1.0 if dtype == "f32" else 1e-2,
+             row_offset_sigma=sigma)
+    say(f"[row offsets] {dtype} D={D} lengths={lengths} sigma={sigma}")
+    check_all(pd, run_gpu(pd), mean_rounding=True)
 
 
 # ---------------------------------------------------------------------------

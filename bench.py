@@ -209,13 +209,17 @@ class Runner:
                 "dshift": torch.empty(p.B, p.D, dtype=tdt, device="cuda")})
         self.ws = torch.empty(max(16, adaln.adaln_bwd_workspace_size(p.B, p.R, p.D, tdt)),
                               dtype=torch.uint8, device="cuda")
+        if p.dense:                         # the [B, N, D] / [B, N] views, made once
+            for s in self.sets:
+                for k in ("x", "dy", "y", "dx"):
+                    s[k + "3"] = s[k].view(p.B, p.N, p.D)
+                for k in ("mean", "rstd"):
+                    s[k + "2"] = s[k].view(p.B, p.N)
 
     def fwd(self, s):
         p, a = self.p, self.adaln
         if p.dense:
-            a.adaln_fwd(s["x"].view(p.B, p.N, p.D), s["shift"], s["scale"], p.eps,
-                        y=s["y"].view(p.B, p.N, p.D), mean=s["mean"].view(p.B, p.N),
-                        rstd=s["rstd"].view(p.B, p.N))
+            a.adaln_fwd(s["x3"], s["shift"], s["scale"], p.eps, y=s["y3"], mean=s["mean2"], rstd=s["rstd2"])
         else:
             a.adaln_fwd_varlen(s["x"], s["shift"], s["scale"], s["offsets"], p.eps, y=s["y"],
                                mean=s["mean"], rstd=s["rstd"])
@@ -223,9 +227,8 @@ class Runner:
     def bwd(self, s):
         p, a = self.p, self.adaln
         if p.dense:
-            self.bwd_fn(s["dy"].view(p.B, p.N, p.D), s["x"].view(p.B, p.N, p.D), s["scale"],
-                        s["mean"].view(p.B, p.N), s["rstd"].view(p.B, p.N), workspace=self.ws,
-                        dx=s["dx"].view(p.B, p.N, p.D), dscale=s["dscale"], dshift=s["dshift"])
+            self.bwd_fn(s["dy3"], s["x3"], s["scale"], s["mean2"], s["rstd2"], workspace=self.ws,
+                        dx=s["dx3"], dscale=s["dscale"], dshift=s["dshift"])
         else:
             a.adaln_bwd_varlen(s["dy"], s["x"], s["scale"], s["mean"], s["rstd"], s["offsets"],
                                workspace=self.ws, dx=s["dx"], dscale=s["dscale"], dshift=s["dshift"])

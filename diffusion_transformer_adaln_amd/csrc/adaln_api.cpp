@@ -154,7 +154,7 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
                       {offsets, offsets ? (B + 1) * 8 : 0}};
   if (any_alias(outs, 4, ins, 6)) return ADALN_ERR_ALIASING;
 
-  const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true);
+  const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true, offsets != nullptr);
   const bool vec = vp.ok && aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(scale);
   if (twopass && !vec) return ADALN_ERR_UNSUPPORTED_SHAPE;
   char* ws = static_cast<char*>(workspace);

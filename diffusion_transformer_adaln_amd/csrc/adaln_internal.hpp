@@ -36,12 +36,14 @@ struct Tiling {
 
 // Row layout of the vectorised kernels: a row of D elements is V = D/EPV
 // 16-byte vectors; LPR lanes cooperate on a row, each holding VPT vectors
-// (vector j*LPR + lane).  NT threads per workgroup hold NT/LPR rows at once.
+// (vector j*LPR + lane).  NT threads per workgroup form NT/LPR row slots, and
+// each slot carries RIF rows per loop iteration.
 struct VecPlan {
   bool ok;
   int vpt;
   int lpr;
   int nt;
+  int rif;
 };
 
 // Largest workgroup of the vectorised kernels: 8 waves, i.e. two per SIMD, so
@@ -49,10 +51,17 @@ struct VecPlan {
 constexpr int VEC_MAX_NT = 512;
 // Rows each slot handles per loop iteration.  Measured on MI355X, one row
 // per slot with more workgroups resident beats deeper per-slot batching or
-// register prefetch: both cost VGPRs, hence occupancy, which is what keeps
-// HBM requests in flight here.
-constexpr int FWD_RIF = 1;
+// register prefetch where a lane holds many elements: both cost VGPRs, hence
+// occupancy, which is what keeps HBM requests in flight here.  The forward's
+// short rows (at most FWD_RIF2_MAX_VPT vectors per lane) take two rows per
+// slot instead: DiT's D = 1152 rows (3 vectors per lane), 8,192 of them, run
+// the forward in 8.1 us at two rows per slot and one iteration per workgroup
+// against 10.3 us at one row per slot and two iterations.
 constexpr int BWD_RIF = 1;
+constexpr int FWD_RIF2_MAX_VPT = 3;
+// dy + x bytes in flight per CU (its backward tiles, one row each) below
+// which a backward workgroup holds two row slots rather than one.
+constexpr int64_t BWD_MIN_CU_BYTES = 32768;
 constexpr int FWD_MAX_VPT = 8;
 constexpr int BWD_MAX_VPT = 4;
 // Tile partial sums are stored chunk-major: for each 16-column chunk, the
@@ -61,8 +70,9 @@ constexpr int BWD_MAX_VPT = 4;
 // finish from 10.0 to 6.4 us on the video shape against a tile-major layout).
 constexpr int PCOLS = 16;
 
-// Vector plan for the forward (backward = false) or backward kernels.
-VecPlan plan_vec(int dtype, int64_t D, bool backward);
+// Vector plan for the forward (backward = false) or backward kernels; varlen
+// selects the packed backward's tiling (more tiles per CU).
+VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen = false);
 
 // Dynamic LDS bytes of a vectorised launch with plan p.
 size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward);

@@ -1063,18 +1063,18 @@ varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile
 // ---------------------------------------------------------------------------
 // Forward grid: many short-lived workgroups keep the rows in flight inside a
 // narrow window of memory; about 128 per CU, but at least two iterations each
-// (measured with streaming accesses: video shape 73 us at two rows per
-// workgroup against 76 at one; mixed-length batch at D = 3072 498 us at 128
-// per CU against 514 at 64 and 540 at 32).
+// at one row per slot (measured with streaming accesses: video shape 73 us at
+// two rows per workgroup against 76 at one; mixed-length batch at D = 3072
+// 498 us at 128 per CU against 514 at 64 and 540 at 32).  At two rows per
+// slot one iteration is enough (DiT, D = 1152: 8.1 us against 11.5 at two).
 constexpr int FWD_WG_PER_CU = 128;
 constexpr int FWD_MIN_ITERS = 2;
 
-template <int DT, int VPT>
+template <int DT, int VPT, int RIF>
 static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* scale, float eps,
                                  const RowMap& rm, int64_t D, const VecPlan& vp, int num_cu,
                                  hipStream_t stream, void* y, float* mean, float* rstd) {
   constexpr int EPV = Elem<DT>::EPV;
-  constexpr int RIF = FWD_RIF;
   const int V = static_cast<int>(D / EPV);
   const int nslots = vp.nt / vp.lpr;
   const size_t lds = vec_lds_bytes(vp, D, false);
@@ -1082,7 +1082,8 @@ static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* s
   const int64_t target = static_cast<int64_t>(num_cu) * FWD_WG_PER_CU;
   int64_t rows_per_wg = (rm.R + target - 1) / target;
   rows_per_wg = ((rows_per_wg + per_iter - 1) / per_iter) * per_iter;
-  if (rows_per_wg < FWD_MIN_ITERS * per_iter) rows_per_wg = FWD_MIN_ITERS * per_iter;
+  const int64_t min_iters = RIF > 1 ? 1 : FWD_MIN_ITERS;
+  if (rows_per_wg < min_iters * per_iter) rows_per_wg = min_iters * per_iter;
   const int64_t grid = (rm.R + rows_per_wg - 1) / rows_per_wg;
   hipLaunchKernelGGL((fwd_vec_kernel<DT, VPT, RIF>), dim3(static_cast<unsigned>(grid)),
                      dim3(vp.nt), lds, stream, static_cast<const uint4*>(x),
@@ -1158,15 +1159,21 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
         return fwd_wave_launch<DT>(x, shift, scale, eps, rm, D, wvpt, active, stream, y, mean, rstd);
       }
     }
+    static_assert(FWD_RIF2_MAX_VPT == 3, "two-row slots are instantiated for VPT 1..3");
+    const bool two = vp.rif == 2 && vp.vpt <= FWD_RIF2_MAX_VPT;
+    if (vp.rif != 1 && !two) return hipErrorInvalidValue;
     switch (vp.vpt) {
-      case 1: return fwd_vec_launch<DT, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 2: return fwd_vec_launch<DT, 2>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 3: return fwd_vec_launch<DT, 3>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 4: return fwd_vec_launch<DT, 4>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 5: return fwd_vec_launch<DT, 5>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 6: return fwd_vec_launch<DT, 6>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 7: return fwd_vec_launch<DT, 7>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
-      case 8: return fwd_vec_launch<DT, 8>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 1: return two ? fwd_vec_launch<DT, 1, 2>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd)
+                         : fwd_vec_launch<DT, 1, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 2: return two ? fwd_vec_launch<DT, 2, 2>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd)
+                         : fwd_vec_launch<DT, 2, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 3: return two ? fwd_vec_launch<DT, 3, 2>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd)
+                         : fwd_vec_launch<DT, 3, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 4: return fwd_vec_launch<DT, 4, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 5: return fwd_vec_launch<DT, 5, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 6: return fwd_vec_launch<DT, 6, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 7: return fwd_vec_launch<DT, 7, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
+      case 8: return fwd_vec_launch<DT, 8, 1>(x, shift, scale, eps, rm, D, vp, num_cu, stream, y, mean, rstd);
       default: return hipErrorInvalidValue;
     }
   }

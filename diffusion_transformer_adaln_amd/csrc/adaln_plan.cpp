@@ -16,49 +16,10 @@ size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
   const int nslots = p.nt / p.lpr;
   const int unit = (p.lpr % 64 == 0) ? 64 : (p.lpr == 32 ? 32 : 16);
   const int groups = p.lpr / unit;
-  const int rif = backward ? BWD_RIF : FWD_RIF;
+  const int rif = p.rif;
   size_t b = groups > 1 || backward ? 2 * static_cast<size_t>(nslots) * rif * groups * 2 * sizeof(float) : 0;
   if (backward && nslots > 1) b += static_cast<size_t>(nslots) * D * sizeof(float);
   return b;
-}
-
-// Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,
-// LPR a multiple of 16.  Measured on MI355X (video shape, D = 5120 bf16):
-//   forward  about 40 elements per lane (two waves per row at D = 5120) with
-//            two rows per workgroup is fastest; one wave per row runs out of
-//            registers, and wide rows of 8-16 elements per lane spend their
-//            time in cross-wave reductions;
-//   backward 16 elements per lane (VPT = 2) keeps the per-column
-//            accumulators, the modulation row and the row data small enough
-//            for four waves per SIMD.
-// Ties prefer rows that cover whole waves (no partial-wave reductions).
-VecPlan plan_vec(int dtype, int64_t D, bool backward) {
-  VecPlan best{false, 0, 0, 0};
-  const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
-  const int epv = dtype == BF16 ? 8 : 4;
-  if (D <= 0 || D % epv != 0) return best;
-  const int64_t V = D / epv;
-  const int want = backward ? 16 : 40;           // elements per lane
-  int best_score = 1 << 30;
-  for (int vpt = 1; vpt <= max_vpt; ++vpt) {
-    if (V % vpt) continue;
-    const int64_t lpr = V / vpt;
-    if (lpr % 16 || lpr > VEC_MAX_NT) continue;
-    VecPlan p{true, vpt, static_cast<int>(lpr), 0};
-    // threads per workgroup: a multiple of both the row lanes and the wave,
-    // at least 128 (short rows share a workgroup)
-    int nt = p.lpr;
-    while (nt % 64) nt += p.lpr;
-    const int min_nt = 128;
-    while (nt < min_nt && nt * 2 <= VEC_MAX_NT) nt *= 2;
-    if (nt > VEC_MAX_NT) continue;
-    p.nt = nt;
-    if (vec_lds_bytes(p, D, backward) > 65536) continue;
-    const int el = vpt * epv;
-    const int score = (el > want ? el - want : want - el) + (lpr % 64 ? 16 : 0);
-    if (score < best_score) { best_score = score; best = p; }
-  }
-  return best;
 }
 
 // Backward tiles per compute unit for dense batches: a tile's column partials
@@ -71,10 +32,68 @@ constexpr int BWD_TILES_PER_CU = 2;
 // 256..32760-row samples at D = 3072: 952 us at two per CU, 907 at four, 927
 // at eight).
 constexpr int BWD_VARLEN_TILES_PER_CU = 4;
+
+// Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,
+// LPR a multiple of 16.  Measured on MI355X (video shape, D = 5120 bf16):
+//   forward  about 40 elements per lane (two waves per row at D = 5120) with
+//            two rows per workgroup is fastest; one wave per row runs out of
+//            registers, and wide rows of 8-16 elements per lane spend their
+//            time in cross-wave reductions;
+//   backward 16 elements per lane (VPT = 2) keeps the per-column
+//            accumulators, the modulation row and the row data small enough
+//            for four waves per SIMD.
+// Ties prefer rows that cover whole waves (no partial-wave reductions).
+VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen) {
+  VecPlan best{false, 0, 0, 0, 1};
+  const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
+  const int epv = dtype == BF16 ? 8 : 4;
+  if (D <= 0 || D % epv != 0) return best;
+  const int64_t V = D / epv;
+  const int want = backward ? 16 : 40;           // elements per lane
+  int best_score = 1 << 30;
+  for (int vpt = 1; vpt <= max_vpt; ++vpt) {
+    if (V % vpt) continue;
+    const int64_t lpr = V / vpt;
+    if (lpr % 16 || lpr > VEC_MAX_NT) continue;
+    const int rif = backward ? BWD_RIF : (vpt <= FWD_RIF2_MAX_VPT ? 2 : 1);
+    VecPlan p{true, vpt, static_cast<int>(lpr), 0, rif};
+    // threads per workgroup: a multiple of both the row lanes and the wave,
+    // at least 128 (short rows share a workgroup)
+    int nt = p.lpr;
+    while (nt % 64) nt += p.lpr;
+    const int min_nt = 128;
+    while (nt < min_nt && nt * 2 <= VEC_MAX_NT) nt *= 2;
+    if (nt > VEC_MAX_NT) continue;
+    // backward: a workgroup of one row slot takes a second slot when the
+    // CU's tiles, one row each, would hold less than BWD_MIN_CU_BYTES of dy
+    // and x in flight.  Dense D = 3072 bf16 (two tiles of 12 KB rows): MMDiT's
+    // 8,192-row image stream 42.6 -> 38.0 us per backward, its 1,024-row text
+    // stream 17.9 -> 15.1 us with 4-row tiles (below).  Packed D = 3072 (four
+    // tiles, 48 KB) was 3% slower with two slots; dense D = 5120 (40 KB) too.
+    const int64_t esize = dtype == BF16 ? 2 : 4;
+    const int64_t tiles_per_cu = varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU;
+    if (backward && nt == p.lpr && tiles_per_cu * 2 * D * esize < BWD_MIN_CU_BYTES &&
+        2 * nt <= VEC_MAX_NT)
+      nt *= 2;
+    p.nt = nt;
+    if (vec_lds_bytes(p, D, backward) > 65536) continue;
+    const int el = vpt * epv;
+    const int score = (el > want ? el - want : want - el) + (lpr % 64 ? 16 : 0);
+    if (score < best_score) { best_score = score; best = p; }
+  }
+  return best;
+}
+
+// Short batches: tiles of at least BWD_MIN_TILE_ROWS rows, so the partial
+// sums (8*D bytes a tile) stay below the rows' own bytes and each workgroup
+// keeps several rows in flight (MMDiT's 1,024-row text stream at D = 3072:
+// 15.1 us per backward with 4-row tiles, 18.3 with 2, 16.4 with 8).
+constexpr int64_t BWD_MIN_TILE_ROWS = 4;
 int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen) {
   const int64_t target =
       static_cast<int64_t>(num_cu) * (varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU);
-  return R <= 0 ? 1 : (R + target - 1) / target;
+  const int64_t rows = R <= 0 ? 1 : (R + target - 1) / target;
+  return rows < BWD_MIN_TILE_ROWS ? BWD_MIN_TILE_ROWS : rows;
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }

@@ -8,7 +8,8 @@
 // its cause, a failing call launches nothing, a valid call launches exactly
 // once with the shape it was given, adaln_bwd_workspace_size() is enough for
 // both backward entry points, and each of them accepts exactly its own
-// workspace layout and rejects one byte less.
+// workspace layout and rejects one byte less.  Also the host planner's
+// invariants that the kernels rely on (row layouts for every D, tilings).
 
 #include <hip/hip_runtime_api.h>
 
@@ -238,7 +239,66 @@ static void test_status_strings() {
   EXPECT(adaln_abi_version() == ADALN_ABI_VERSION, "ABI version mismatch");
 }
 
+// The planner's invariants that the kernels rely on, for every row width up
+// to the largest supported D: a vector plan covers the row exactly with lane
+// groups the reductions handle, fits one workgroup and its LDS, and carries
+// two rows per slot only where the forward instantiates that; the backward's
+// tiling puts every tile inside the partial-sum buffer it sizes.
+static void test_plans() {
+  for (int dt : {adaln::F32, adaln::BF16}) {
+    const int64_t epv = dt == adaln::BF16 ? 8 : 4;
+    for (int64_t D = 1; D <= ADALN_MAX_D; ++D) {
+      for (int dir = 0; dir < 3; ++dir) {   // forward, dense backward, packed backward
+        const bool bwd = dir > 0;
+        const adaln::VecPlan p = adaln::plan_vec(dt, D, bwd, dir == 2);
+        if (!p.ok) continue;   // the general kernels take these widths
+        const int64_t V = D / epv;
+        const bool shape_ok = p.vpt >= 1 && p.vpt <= (bwd ? adaln::BWD_MAX_VPT : adaln::FWD_MAX_VPT) &&
+                              D % epv == 0 && static_cast<int64_t>(p.vpt) * p.lpr == V && p.lpr % 16 == 0;
+        const bool wg_ok = p.nt >= p.lpr && p.nt % p.lpr == 0 && p.nt % 64 == 0 && p.nt <= adaln::VEC_MAX_NT;
+        const bool rif_ok = bwd ? p.rif == adaln::BWD_RIF
+                                : (p.rif == 1 || (p.rif == 2 && p.vpt <= adaln::FWD_RIF2_MAX_VPT));
+        const bool lds_ok = adaln::vec_lds_bytes(p, D, bwd) <= 65536;
+        EXPECT(shape_ok && wg_ok && rif_ok && lds_ok, "plan dtype %d D %lld dir %d: vpt %d lpr %d nt %d rif %d",
+               dt, (long long)D, dir, p.vpt, p.lpr, p.nt, p.rif);
+      }
+    }
+  }
+  // the workloads' row widths, and the widest rows the GPU tests use, are vectorised
+  const struct { int dt; int64_t D; } want[] = {{adaln::F32, 128}, {adaln::BF16, 1152}, {adaln::BF16, 3072},
+                                               {adaln::BF16, 5120}, {adaln::BF16, 16384}, {adaln::F32, 4096}};
+  for (const auto& w : want)
+    for (int dir = 0; dir < 3; ++dir)
+      EXPECT(adaln::plan_vec(w.dt, w.D, dir > 0, dir == 2).ok, "no vector plan for dtype %d D %lld dir %d", w.dt,
+             (long long)w.D, dir);
+  const int64_t Bs[] = {1, 2, 3, 8, 277};
+  const int64_t Ns[] = {0, 1, 2, 3, 5, 64, 100, 512, 1023, 4096, 18900, 64000};
+  const int cus_list[] = {1, 80, 256, 304};
+  for (int cus : cus_list)
+    for (int64_t B : Bs)
+      for (int64_t N : Ns)
+        for (int64_t D : {int64_t(8), int64_t(1152), int64_t(5120)}) {
+          const int64_t R = B * N;
+          for (int varlen = 0; varlen < 2; ++varlen) {
+            const adaln::WorkspaceLayout w = adaln::bwd_workspace_layout(B, R, D, cus, varlen, N);
+            const int64_t dense_tiles = B * ((N + w.tile_rows - 1) / w.tile_rows);
+            const size_t chunks = static_cast<size_t>((D + adaln::PCOLS - 1) / adaln::PCOLS);
+            const bool ok =
+                w.tile_rows >= 1 && (R == 0 || w.tile_rows >= 4) &&
+                w.tiles_alloc >= (R + w.tile_rows - 1) / w.tile_rows + B &&   // any split into B samples
+                w.tiles_max <= w.tiles_alloc && (varlen || w.tiles_max == dense_tiles) &&
+                w.partial_off % 256 == 0 && w.partial_off >= static_cast<size_t>(B + 1) * 8 &&
+                w.total >= w.partial_off + chunks * static_cast<size_t>(w.tiles_alloc) * 2 * adaln::PCOLS * 4 &&
+                adaln::bwd_workspace_bytes(B, R, D, cus) >= w.total;
+            EXPECT(ok, "tiling B %lld N %lld D %lld cus %d varlen %d: tile_rows %lld tiles %lld/%lld", (long long)B,
+                   (long long)N, (long long)D, cus, varlen, (long long)w.tile_rows, (long long)w.tiles_max,
+                   (long long)w.tiles_alloc);
+          }
+        }
+}
+
 int main() {
+  test_plans();
   test_forward();
   test_forward_varlen();
   test_backward();

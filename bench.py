@@ -49,6 +49,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -552,14 +553,31 @@ def read_traffic(path, config):
 OPERATOR_SOURCES = ("adaln_api.cpp", "adaln_internal.hpp", "adaln_kernels.hip", "adaln_plan.cpp")
 
 
+# string literal | character literal | line comment | block comment
+_CODE_TOKENS = re.compile(r"""
+    "(?:\\.|[^"\\\n])*"
+  | '(?:\\.|[^'\\\n])*'
+  | //[^\n]*
+  | /\*.*?\*/
+""", re.S | re.X)
+
+
+def _code_only(text):
+    """C++ source without comments, blank lines and indentation (string and
+    character literals kept), so that editing a comment leaves the hash alone."""
+    text = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_sha():
+    """sha256 prefix over the operator's sources, comments and layout removed."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "diffusion_transformer_adaln_amd", "csrc")
     for name in OPERATOR_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,6 +16,10 @@
 //     load of a row is one contiguous 16*LPR-byte span.  A workgroup of NT
 //     threads works on NT/LPR rows at a time ("slots"), and each slot keeps
 //     RIF rows in flight per iteration.
+//   * Rows of exactly 64 lanes x at most 10 vectors take a persistent forward
+//     instead: one wave per row, a fixed grid of about four waves per CU
+//     walking the rows grid-stride, each wave loading its next row into
+//     registers while it reduces and writes the current one.
 //   * Row reductions run in three fixed-order stages: a 16-lane butterfly
 //     with DPP (quad_perm, row_half_mirror, row_mirror), cross-row lane
 //     exchanges inside the wave, then LDS across the waves or 16-lane groups
@@ -28,8 +32,9 @@
 //   * The backward keeps each lane's column partial sums of dy and dy*xhat in
 //     registers over a tile of rows inside one sample, combines the slots of a
 //     workgroup through LDS in slot order, and writes them once per tile,
-//     coalesced along D.  A finish kernel adds a sample's tiles in ascending
-//     tile order.  No floating-point atomics anywhere: bitwise repeatable.
+//     coalesced along D.  A finish kernel adds a sample's tiles in an order
+//     fixed by the shape and the CU count.  No floating-point atomics
+//     anywhere: bitwise repeatable.
 //
 // General kernels (any D, any alignment) cover the shapes the vector layout
 // cannot; they compute the same quantities with scalar accesses.

@@ -7,7 +7,8 @@ independent library routine:
 
   * torch's fp64 LayerNorm (scale = shift = 0 special case) and autograd,
   * closed forms and invariants of the normalised rows and of dx,
-  * central finite differences of L = sum(y * dy),
+  * central finite differences of L = sum(y * dy), and explicit per-row
+    Jacobians of the forward by finite differences against torch's,
   * hand-derived worked examples,
   * exact special cases (scale = -1, dy = 1, constant rows, empty samples),
   * the page's bucket rule evaluated by hand (AdaptiveLoad summary, section 2.A).
@@ -201,6 +202,42 @@ def check_finite_differences(impl):
                 _close(grad, fd, 1e-6, 1e-7, f"finite differences d{name} D={D} eps={eps}")
 
 
+def check_explicit_jacobian(impl):
+    """Per row, the D x D Jacobian of y with respect to x, by central
+    differences of the oracle's forward, equals torch fp64 autograd's Jacobian
+    of layer_norm(x) * (1 + scale) + shift; it sends a constant shift of the
+    row to zero (J @ 1 = 0); and the oracle's dx is J^T dy for several dy."""
+    D = 6
+    lengths = (2, 1)
+    one_row = np.array([0, 1], dtype=np.int64)
+    g = _rng(82)
+    h = 1e-6
+    for eps in (1e-6, 1e-2):
+        x, shift, scale, _, _ = _case(81, lengths, D, outliers=False)
+        for r in range(x.shape[0]):
+            b = 0 if r < lengths[0] else 1
+
+            def f(v):
+                y, _, _ = impl.adaln_fwd(v[None, :], shift[b:b + 1], scale[b:b + 1], eps, one_row)
+                return y[0]
+
+            J = np.zeros((D, D))
+            for j in range(D):
+                e = np.zeros(D)
+                e[j] = h
+                J[:, j] = (f(x[r] + e) - f(x[r] - e)) / (2 * h)
+            sc_t, sh_t = torch.as_tensor(scale[b]), torch.as_tensor(shift[b])
+            Jt = torch.autograd.functional.jacobian(
+                lambda v: torch.nn.functional.layer_norm(v, (D,), None, None, eps) * (1.0 + sc_t) + sh_t,
+                torch.as_tensor(x[r])).numpy()
+            _close(J, Jt, 1e-6, 1e-7, f"Jacobian row {r} eps={eps}")
+            _close(J @ np.ones(D), np.zeros(D), 0.0, 1e-6, f"J @ 1 row {r} eps={eps}")
+            for _ in range(3):
+                dy = g.standard_normal((1, D))
+                dx, _, _ = impl.adaln_bwd(dy, x[r:r + 1], scale[b:b + 1], eps, one_row)
+                _close(dx[0], Jt.T @ dy[0], 1e-10, 1e-12, f"dx = J^T dy row {r} eps={eps}")
+
+
 def check_torch_autograd(impl):
     """dx, dscale, dshift equal torch fp64 autograd of layer_norm(x)*(1+scale[b])+shift[b]."""
     D = 24
@@ -319,6 +356,7 @@ CHECKS = [
     check_affine_invariance,
     check_constant_row,
     check_finite_differences,
+    check_explicit_jacobian,
     check_torch_autograd,
     check_dx_closed_forms,
     check_dy_constant,

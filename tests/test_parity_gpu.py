@@ -105,6 +105,42 @@ def test_shapes(dtype, D, lengths):
         check_all(pd, run_gpu(pd, dense=False))
 
 
+# The fuzz grid: every D here against one-row, tiny, one-wave-plus and
+# several-thousand-row batches, both dtypes.  The 4,097-row batches are
+# checked on sampled rows and on every sample's full column sums.
+FUZZ_D = [1, 7, 64, 127, 768, 1152, 3072, 4096, 5120, 8192]
+FUZZ_BN = [(1, 1), (3, 3), (1, 255), (3, 4097)]
+FUZZ = [(dt, D, B, N) for dt in ("f32", "bf16") for D in FUZZ_D for B, N in FUZZ_BN]
+
+
+@pytest.mark.parametrize("dtype,D,B,N", FUZZ, ids=[f"{dt}-D{D}-B{B}xN{N}" for dt, D, B, N in FUZZ])
+def test_fuzz_grid(dtype, D, B, N):
+    pd = _pd(dtype, D, [N] * B, seed=1000 + D + N, dy_sigma=1.0 if dtype == "f32" else 1e-2)
+    say(f"[fuzz] {dtype} D={D} B={B} N={N}")
+    out = run_gpu(pd)
+    if B * N <= 1024:
+        check_all(pd, out)
+    else:
+        check_rows(pd, out, sampled_rows(pd))
+        check_samples(pd, out, np.arange(B))
+
+
+# eps = 0 (pure LayerNorm scaling; the rows here are never constant) and a
+# large eps, on each forward kernel: one wave per row (D = 5120), slots
+# (D = 1152), general (D = 100), fp32 slots (D = 768).
+EPS_CASES = [("bf16", 5120, [40]), ("bf16", 1152, [3, 30]), ("bf16", 100, [17]), ("f32", 768, [33])]
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-2])
+@pytest.mark.parametrize("dtype,D,lengths", EPS_CASES, ids=[f"{d}-D{D}" for d, D, _ in EPS_CASES])
+def test_eps_values(dtype, D, lengths, eps):
+    pd = _pd(dtype, D, lengths, seed=31 + D, dy_sigma=1.0 if dtype == "f32" else 1e-2)
+    say(f"[eps] {dtype} D={D} lengths={lengths} eps={eps}")
+    check_all(pd, run_gpu(pd, eps=eps), eps=eps)
+    if len(lengths) > 1:
+        check_all(pd, run_gpu(pd, eps=eps, dense=False), eps=eps)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_misaligned_pointers_take_general_path(dtype):
     import diffusion_transformer_adaln_amd as adaln
@@ -196,7 +232,7 @@ def test_run_to_run_bitwise(dtype, D, lengths):
     pd = _pd(dtype, D, lengths, seed=21)
     say(f"[determinism] {dtype} D={D} lengths={lengths}")
     ref = None
-    for _ in range(10):
+    for _ in range(20):
         out = run_gpu(pd)
         h = {k: hashlib.sha256(bits(v)).hexdigest() for k, v in out.items()}
         if ref is None:

@@ -533,16 +533,15 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   const int buf_stride = nslots * RIF * groups;
   const float inv_d = 1.0f / static_cast<float>(D);
 
-  float sc1[VPT][EPV];
+  // The modulation row, requested first and unpacked after the first rows
+  // are requested (below).
+  uint4 sc_raw[VPT];
   {
     const uint4* scp = scale + b * V + lane;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      E::unpack(scp[j * lpr], sc1[j]);
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
-    }
+    for (int j = 0; j < VPT; ++j) sc_raw[j] = scp[j * lpr];
   }
+  float sc1[VPT][EPV];
   float acc_h[VPT][EPV], acc_s[VPT][EPV];   // column partials of dy and dy*xhat
 #pragma unroll
   for (int j = 0; j < VPT; ++j)
@@ -570,9 +569,8 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   };
 
   const int64_t rows_per_iter = static_cast<int64_t>(nslots) * RIF;
-  int it = 0;
-  for (int64_t base = 0; base < count; base += rows_per_iter, ++it) {
-    load_rows(base, xv, gv, mu, rs);
+  // One loop iteration after its rows were requested; `it` picks the LDS buffer.
+  auto process = [&](int64_t base, int it) {
 
     float sg[RIF], sgx[RIF];
 #pragma unroll
@@ -636,6 +634,23 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
         store_stream(dxr + j * lpr, E::pack(out));
       }
     }
+  };
+  // The first iteration is peeled: its rows are requested before the
+  // modulation row is unpacked, so the two share one memory round trip (a
+  // tile has at least one row).
+  load_rows(0, xv, gv, mu, rs);
+  __builtin_amdgcn_sched_barrier(0);   // every first-row load ahead of the wait below
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    E::unpack(sc_raw[j], sc1[j]);
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
+  }
+  process(0, 0);
+  int it = 1;
+  for (int64_t base = rows_per_iter; base < count; base += rows_per_iter, ++it) {
+    load_rows(base, xv, gv, mu, rs);
+    process(base, it);
   }
   if (!COLS) return;
 

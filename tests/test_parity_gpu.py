@@ -4,8 +4,8 @@ Small problems (several tiles plus a ragged tail) are checked in full;
 the full-size workloads are checked on sampled rows and on whole-sample
 column sums.  Edge cases: empty inputs and samples, one-row samples, odd and
 tiny D, misaligned pointers (general kernels), the largest supported D,
-constant rows, rows far from zero mean, determinism and dense/packed
-equivalence.
+more than 2^31 elements in one tensor, constant rows, rows far from zero
+mean, determinism and dense/packed equivalence.
 """
 
 import hashlib
@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from gpu_helpers import (bits, check_all, check_rows, check_samples, run_gpu, sampled_rows, say,
                          to_dev)
@@ -139,6 +140,62 @@ def test_eps_values(dtype, D, lengths, eps):
     check_all(pd, run_gpu(pd, eps=eps), eps=eps)
     if len(lengths) > 1:
         check_all(pd, run_gpu(pd, eps=eps, dense=False), eps=eps)
+
+
+def test_more_than_2pow31_elements():
+    """A dense batch of 700,416 rows x 3072 bf16 (2.15e9 elements per tensor,
+    past any 32-bit element index): 684 copies of one seeded 1,024-row block,
+    laid out on the device, so the oracle checks rows sampled across the whole
+    batch against the block's rows and each column sum against 684 times the
+    block's (computed in fp64)."""
+    import diffusion_transformer_adaln_amd as adaln
+    from gpu_helpers import TOL, assert_rel_floored, to_host64
+
+    D, NB, REP = 3072, 1024, 684
+    N = NB * REP
+    assert N * D > 2 ** 31
+    pd = _pd("bf16", D, [NB], seed=77, dy_sigma=1e-2)
+    p = pd.problem
+    say(f"[2^31] bf16 B=1 N={N} D={D}")
+    x = to_dev(pd.x, "bf16").repeat(REP, 1).view(1, N, D)
+    dy = to_dev(pd.dy, "bf16").repeat(REP, 1).view(1, N, D)
+    shift, scale = to_dev(pd.shift, "bf16"), to_dev(pd.scale, "bf16")
+    y, mean, rstd = adaln.adaln_fwd(x, shift, scale, p.eps)
+    dx, ds, dh = adaln.adaln_bwd(dy, x, scale, mean, rstd)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(5))
+    big = np.unique(np.concatenate([g.choice(N, 64, replace=False),
+                                    [0, 1, N - 1, 2 ** 31 // D, 2 ** 31 // D + 1]])).astype(np.int64)
+    idx = torch.from_numpy(big).cuda()
+    got = {"y": y.view(N, D).index_select(0, idx), "dx": dx.view(N, D).index_select(0, idx),
+           "mean": mean.view(N).index_select(0, idx), "rstd": rstd.view(N).index_select(0, idx)}
+    # every repeat of a block row gives the same bits
+    blk = big % NB
+    for k, v in got.items():
+        first = {}
+        for i, r in enumerate(blk.tolist()):
+            if r in first:
+                assert torch.equal(v[i], v[first[r]]), f"{k}: repeats of block row {r} differ"
+            else:
+                first[r] = i
+    # the block's rows against the oracle
+    keep = np.array(sorted(first.values()))
+    out = {"y": torch.zeros(NB, D, dtype=torch.bfloat16, device="cuda"),
+           "dx": torch.zeros(NB, D, dtype=torch.bfloat16, device="cuda"),
+           "mean": torch.zeros(NB, device="cuda"), "rstd": torch.zeros(NB, device="cuda")}
+    bidx = torch.from_numpy(blk[keep]).cuda()
+    kidx = torch.from_numpy(keep).cuda()
+    for k in out:
+        out[k].index_copy_(0, bidx, got[k].index_select(0, kidx))
+    res = check_rows(pd, out, blk[keep])
+    # column sums: REP times the block's
+    xo, dyo = oracle.decode(pd.x, "bf16"), oracle.decode(pd.dy, "bf16")
+    _, ds_ref, dh_ref = oracle.adaln_bwd(dyo, xo, oracle.decode(pd.scale, "bf16"), p.eps, pd.offsets)
+    res["dscale_rel"] = assert_rel_floored(to_host64(ds), REP * ds_ref, TOL["bf16"]["rel"], "dscale")
+    res["dshift_rel"] = assert_rel_floored(to_host64(dh), REP * dh_ref, TOL["bf16"]["rel"], "dshift")
+    say(f"  rows={keep.size} {res}")
+    del x, dy, y, dx, mean, rstd
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -26,7 +26,8 @@ algorithmic bytes per call / mean call duration from HIP events recorded on
 the launch stream right after the timed region, one event pair around each
 block of ten back-to-back calls (each timing event stalls the queue for a
 few microseconds, which is why none sits inside the timed region and why a
-pair does not bracket a single call).
+pair does not bracket a single call); `per_call_us` gives the 10th, 50th and
+90th percentiles of those block means for the forward and the backward.
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
 
@@ -519,6 +520,9 @@ def main():
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
         "bwd_us": round(float(bwd_ms.mean()) * 1e3, 2),
+        "per_call_us": {k: {f"p{q}": round(float(np.percentile(v, q)) * 1e3, 2) for q in (10, 50, 90)}
+                        | {"blocks": int(v.size), "calls_per_block": BLOCK}
+                        for k, v in (("fwd", fwd_ms), ("bwd", bwd_ms))},
         "fwd_gbs": round(fwd_gbs, 1),
         "algorithmic_bytes_per_step": nbytes["total"],
         "activation_bytes": {"saved": act, "what": act_note},

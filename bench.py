@@ -167,11 +167,19 @@ def cpu_baseline(pd, seconds):
     import workloads
 
     per_row = workloads.algorithmic_bytes(p)["total"] / p.R
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {
         "value": round(rows_done * per_row / t_used / 1e9, 4),
         "unit": "GB/s",
         "rows_per_s": round(rows_done / t_used, 1),
         "cores": 1,
+        "cores_available": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"fp64 oracle fwd+bwd over {rows_done} rows of {p.name} (D={p.D}, "
                   f"{rows_done / p.R:.2f} passes over its {p.R} rows), 128-row blocks, "

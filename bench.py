@@ -28,6 +28,8 @@ block of ten back-to-back calls (each timing event stalls the queue for a
 few microseconds, which is why none sits inside the timed region and why a
 pair does not bracket a single call); `per_call_us` gives the 10th, 50th and
 90th percentiles of those block means for the forward and the backward.
+`device` records the GPU's name, architecture, CU count and memory (a
+partitioned device shows fewer CUs and a slice of the bandwidth).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload's rows on one host core.
 
@@ -505,6 +507,7 @@ def main():
     if args.impl == "torch":
         bwd_name = "eager PyTorch autograd backward"
 
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
     out = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -524,6 +527,9 @@ def main():
                        f"D={r.p.D}, {r.p.dtype} I/O, fp32 statistics" for r in runners),
                    "name": args.config, "B": sum(r.p.B for r in runners), "rows": rows,
                    "D": p.D, "impl": args.impl, "bwd": bwd_name, "parallelism": "single GPU"},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count,
+                   "hbm_gib": round(props.total_memory / 2 ** 30, 1)},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),

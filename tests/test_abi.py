@@ -122,3 +122,50 @@ def test_workspace_query_rejects_bad_sizes(lib):
     assert lib.adaln_bwd_workspace_size(1, -1, 8, 1) == 0
     assert lib.adaln_bwd_workspace_size(1, 10, 0, 1) == 0
     assert lib.adaln_bwd_workspace_size(1, 10, 8, 5) == 0
+
+
+def test_headers_compile_as_c_and_link(tmp_path, lib):
+    """A plain C11 program includes both headers, links libadaln.so and calls
+    the host-only entry points: the ABI is usable from C without torch."""
+    import shutil
+
+    cc = shutil.which("gcc")
+    if cc is None or not os.path.isfile("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("needs gcc and the HIP runtime headers")
+    src = tmp_path / "consumer.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "adaln.h"
+#include "adaln_sched.h"
+int main(void) {
+  if (adaln_abi_version() != ADALN_ABI_VERSION) return 1;
+  if (adaln_status_str(ADALN_ERR_ALIASING) == NULL) return 2;
+  /* the pages' bucket rule at M_mem = 65536, M_comp = 2^30, p = 2: S = 4096 -> 16 */
+  if (adaln_sched_batch_size(4096, 65536, (int64_t)1 << 30, 2.0) != 16) return 3;
+  {
+    const double load[4] = {1.0, 1.0, 1.0, 1.0};
+    if (adaln_load_cv(load, 4) != 0.0) return 4;
+  }
+  /* every entry point is a linkable symbol */
+  {
+    typedef void (*fn_t)(void);
+    fn_t fns[] = {(fn_t)adaln_fwd, (fn_t)adaln_bwd, (fn_t)adaln_fwd_varlen, (fn_t)adaln_bwd_varlen,
+                  (fn_t)adaln_bwd_twopass, (fn_t)adaln_bwd_workspace_size, (fn_t)adaln_sched_plan,
+                  (fn_t)adaln_cost_fit};
+    for (int i = 0; i < 8; ++i) if (fns[i] == NULL) return 5;
+  }
+  puts("ok");
+  return 0;
+}
+''')
+    exe = str(tmp_path / "consumer")
+    libdir = os.path.dirname(LIB_PATH)
+    # strict ISO C for this library's headers; ROCm's own headers (hipStream_t) come in
+    # as system headers, since they are not pedantic-clean C themselves
+    build = subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-pedantic-errors", "-D__HIP_PLATFORM_AMD__",
+                            "-isystem", "/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), str(src), "-o", exe,
+                            "-L" + libdir, "-ladaln", "-Wl,-rpath," + libdir],
+                           capture_output=True, text=True, timeout=120)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.returncode, run.stdout, run.stderr[-2000:])

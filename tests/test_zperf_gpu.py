@@ -2,7 +2,7 @@
 workloads must reach at least 85% of the last accepted GB/s on one MI355X
 (box-to-box spread of the same kernels is about 3%).  Each run is bench.py
 itself, in a child process, so the guard times exactly what the bench line
-reports."""
+reports; the line's fields and roofline arithmetic are checked too."""
 
 import json
 import os
@@ -31,3 +31,14 @@ def test_bench_throughput_floor(config):
     print(f"  {res['value']} GB/s ({res['pct_of_peak']}% of peak), {res['ms_per_step']} ms/step", flush=True)
     assert res["value"] >= FLOOR * ACCEPTED_GBS[config], (
         f"{config}: {res['value']} GB/s is below {FLOOR:.0%} of the accepted {ACCEPTED_GBS[config]} GB/s")
+    # the line's contract
+    for k, t in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
+                 ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
+                 ("dtype", str), ("data", str), ("config", dict), ("roofline", dict)):
+        assert isinstance(res.get(k), t), f"{k}: {res.get(k)!r}"
+    assert "vs_baseline" in res and res["n_gpus"] == 1 and res["steps"] == 50
+    assert res["config"]["name"] == config and isinstance(res["config"]["workload"], str)
+    rf = res["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and 0.0 < rf["frac"] < 1.0
+    assert "traffic" in rf

@@ -46,7 +46,7 @@ int64_t esize(adaln_dtype_t dt) { return dt == ADALN_BF16 ? 2 : 4; }
 
 bool dtype_ok(adaln_dtype_t dt) { return dt == ADALN_F32 || dt == ADALN_BF16; }
 
-// a*b*c (each >= 0) without int64 overflow
+// a*b (both >= 0) without int64 overflow
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a != 0 && b > INT64_MAX / a) return false;
   *out = a * b;

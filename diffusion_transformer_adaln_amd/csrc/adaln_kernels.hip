@@ -315,12 +315,24 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 
   float sc1[VPT][EPV], sh[VPT][EPV];
   int64_t cur_lo = 0, cur_hi = 0;     // rows of the sample whose modulation is loaded
-  int it = 0;
-
-  for (int64_t base = r_begin; base < r_end; base += rows_per_iter, ++it) {
-    uint4 xv[RIF][VPT];
-    int64_t row[RIF];
-    bool valid[RIF];
+  auto load_mod = [&](int64_t r) {    // unpacked 1 + scale and shift of row r's sample
+    const int64_t b = sample_of_row(rm, r);
+    cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
+    cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
+    const uint4* scp = scale + b * V + lane;
+    const uint4* shp = shift + b * V + lane;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      E::unpack(scp[j * lpr], sc1[j]);
+      E::unpack(shp[j * lpr], sh[j]);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
+    }
+  };
+  uint4 xv[RIF][VPT];
+  int64_t row[RIF];
+  bool valid[RIF];
+  auto load_x = [&](int64_t base) {
 #pragma unroll
     for (int i = 0; i < RIF; ++i) {
       row[i] = base + static_cast<int64_t>(slot) * RIF + i;
@@ -329,7 +341,9 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
       for (int j = 0; j < VPT; ++j) xv[i][j] = valid[i] ? load_stream(xr + j * lpr) : make_uint4(0, 0, 0, 0);
     }
-
+  };
+  // One iteration after its rows were requested; `it` picks the LDS buffer.
+  auto process = [&](int it) {
     // per-lane two-pass (mean, M2), then the fixed-order merge across lanes
     float m[RIF], s[RIF];
 #pragma unroll
@@ -377,20 +391,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
       if (!valid[i]) continue;
       const float rs = 1.0f / sqrtf(s[i] * inv_d + eps);
       if (lane == 0) { mean[row[i]] = m[i]; rstd[row[i]] = rs; }
-      if (row[i] >= cur_hi || row[i] < cur_lo) {
-        const int64_t b = sample_of_row(rm, row[i]);
-        cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
-        cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
-        const uint4* scp = scale + b * V + lane;
-        const uint4* shp = shift + b * V + lane;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-          E::unpack(scp[j * lpr], sc1[j]);
-          E::unpack(shp[j * lpr], sh[j]);
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
-        }
-      }
+      if (row[i] >= cur_hi || row[i] < cur_lo) load_mod(row[i]);
       uint4* yr = y + row[i] * V + lane;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
@@ -403,6 +404,26 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
         }
         store_stream(yr + j * lpr, E::pack(f));
       }
+    }
+    };
+
+  if constexpr (RIF > 1) {
+    // Two rows per slot: typically one iteration per workgroup, so the first
+    // rows and their sample's modulation are requested together (one memory
+    // round trip instead of two; r_begin < R).
+    load_x(r_begin);
+    load_mod(r_begin);
+    process(0);
+    int it = 1;
+    for (int64_t base = r_begin + rows_per_iter; base < r_end; base += rows_per_iter, ++it) {
+      load_x(base);
+      process(it);
+    }
+  } else {
+    int it = 0;
+    for (int64_t base = r_begin; base < r_end; base += rows_per_iter, ++it) {
+      load_x(base);
+      process(it);
     }
   }
 }

@@ -10,8 +10,10 @@ from ._lib import (  # noqa: F401
     AdaLNError,
     adaln_abi_version,
     adaln_bwd,
+    adaln_bwd_f32sums,
     adaln_bwd_twopass,
     adaln_bwd_varlen,
+    adaln_bwd_varlen_f32sums,
     adaln_bwd_workspace_size,
     adaln_cost_fit,
     adaln_fwd,

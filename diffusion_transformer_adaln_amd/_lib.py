@@ -34,6 +34,8 @@ EXPORTED = (
     "adaln_fwd_varlen",
     "adaln_bwd_varlen",
     "adaln_bwd_twopass",
+    "adaln_bwd_f32sums",
+    "adaln_bwd_varlen_f32sums",
     "adaln_bwd_workspace_size",
     "adaln_status_str",
     "adaln_abi_version",
@@ -76,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_bwd.restype = ctypes.c_int
     lib.adaln_bwd_twopass.argtypes = lib.adaln_bwd.argtypes
     lib.adaln_bwd_twopass.restype = ctypes.c_int
+    lib.adaln_bwd_f32sums.argtypes = lib.adaln_bwd.argtypes
+    lib.adaln_bwd_f32sums.restype = ctypes.c_int
     lib.adaln_sched_batch_size.argtypes = [_I64, _I64, _I64, ctypes.c_double]
     lib.adaln_sched_batch_size.restype = _I64
     lib.adaln_sched_plan.argtypes = [_P, _I64, _I64, _I64, ctypes.c_double, _P, _P]
@@ -88,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P,
                                      ctypes.c_size_t, _P, _P, _P, _P]
     lib.adaln_bwd_varlen.restype = ctypes.c_int
+    lib.adaln_bwd_varlen_f32sums.argtypes = lib.adaln_bwd_varlen.argtypes
+    lib.adaln_bwd_varlen_f32sums.restype = ctypes.c_int
     lib.adaln_bwd_workspace_size.argtypes = [_I64, _I64, _I64, ctypes.c_int]
     lib.adaln_bwd_workspace_size.restype = ctypes.c_size_t
     lib.adaln_status_str.argtypes = [ctypes.c_int]
@@ -237,6 +243,14 @@ def adaln_bwd(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, ds
     return _bwd_dense("adaln_bwd", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
 
 
+def adaln_bwd_f32sums(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, dshift=None,
+                      stream=None):
+    """adaln_bwd with dscale and dshift in float32 whatever x's dtype (for sums
+    that are added to others before rounding)."""
+    return _bwd_dense("adaln_bwd_f32sums", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift,
+                      stream, torch.float32)
+
+
 def adaln_bwd_twopass(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=None, dshift=None,
                       stream=None):
     """The same backward with the column reduction as a separate D-tile pass
@@ -244,13 +258,14 @@ def adaln_bwd_twopass(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=
     return _bwd_dense("adaln_bwd_twopass", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
 
 
-def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream):
+def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream, sums_dtype=None):
     if x.dim() != 3 or dy.shape != x.shape:
         raise ValueError(f"{fn} expects dy and x of shape [B, N, D]")
     B, N, D = x.shape
+    sums_dtype = x.dtype if sums_dtype is None else sums_dtype
     dx = torch.empty_like(x) if dx is None else dx
-    dscale = torch.empty((B, D), dtype=x.dtype, device=x.device) if dscale is None else dscale
-    dshift = torch.empty((B, D), dtype=x.dtype, device=x.device) if dshift is None else dshift
+    dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
+    dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
     dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
     if mean.dtype != torch.float32 or rstd.dtype != torch.float32:
         raise TypeError("mean and rstd must be float32")
@@ -266,22 +281,36 @@ def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stre
 def adaln_bwd_varlen(dy, x, scale, mean, rstd, offsets, workspace=None, dx=None, dscale=None, dshift=None,
                      stream=None):
     """Backward of packed samples.  Returns (dx [R, D], dscale [B, D], dshift [B, D])."""
+    return _bwd_varlen("adaln_bwd_varlen", dy, x, scale, mean, rstd, offsets, workspace, dx, dscale,
+                       dshift, stream)
+
+
+def adaln_bwd_varlen_f32sums(dy, x, scale, mean, rstd, offsets, workspace=None, dx=None, dscale=None,
+                             dshift=None, stream=None):
+    """adaln_bwd_varlen with dscale and dshift in float32 whatever x's dtype."""
+    return _bwd_varlen("adaln_bwd_varlen_f32sums", dy, x, scale, mean, rstd, offsets, workspace, dx,
+                       dscale, dshift, stream, torch.float32)
+
+
+def _bwd_varlen(fn, dy, x, scale, mean, rstd, offsets, workspace, dx, dscale, dshift, stream,
+                sums_dtype=None):
     if x.dim() != 2 or dy.shape != x.shape:
-        raise ValueError("adaln_bwd_varlen expects dy and x of shape [R, D]")
+        raise ValueError(f"{fn} expects dy and x of shape [R, D]")
     R, D = x.shape
     B = scale.shape[0]
     if offsets.shape != (B + 1,) or offsets.dtype != torch.int64:
         raise ValueError("offsets must be int64 [B+1]")
+    sums_dtype = x.dtype if sums_dtype is None else sums_dtype
     dx = torch.empty_like(x) if dx is None else dx
-    dscale = torch.empty((B, D), dtype=x.dtype, device=x.device) if dscale is None else dscale
-    dshift = torch.empty((B, D), dtype=x.dtype, device=x.device) if dshift is None else dshift
+    dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
+    dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
     dev = _check_dev(dy, x, scale, mean, rstd, offsets, dx, dscale, dshift)
     lib = load_library()
     workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace)
-    st = _on(dev, lib.adaln_bwd_varlen, _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd),
+    st = _on(dev, getattr(lib, fn), _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd),
              _ptr(offsets), B, R, D, _dtype_code(x.dtype), _ptr(workspace), wbytes,
              _stream(dev, stream), _ptr(dx), _ptr(dscale), _ptr(dshift))
-    _raise("adaln_bwd_varlen", st)
+    _raise(fn, st)
     return dx, dscale, dshift
 
 

@@ -80,6 +80,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Sizes {
   int64_t R, row_bytes_total, mod_bytes, stat_bytes;
+  int64_t sum_bytes_f32;   // a [B, D] fp32 column-sum output
 };
 
 // Shared shape checks.  R = total rows.
@@ -87,14 +88,16 @@ adaln_status_t check_shape(int64_t B, int64_t R, int64_t D, adaln_dtype_t dt, Si
   if (!dtype_ok(dt)) return ADALN_ERR_UNSUPPORTED_DTYPE;
   if (B < 1 || R < 0 || D < 1) return ADALN_ERR_INVALID_ARG;
   if (D > ADALN_MAX_D) return ADALN_ERR_UNSUPPORTED_SHAPE;
-  int64_t rd, rdb, bd, bdb, rs;
+  int64_t rd, rdb, bd, bdb, bd4, rs;
   if (!mul_ok(R, D, &rd) || !mul_ok(rd, esize(dt), &rdb) || !mul_ok(B, D, &bd) ||
-      !mul_ok(bd, esize(dt), &bdb) || !mul_ok(R, 4, &rs) || rd > (INT64_MAX >> 8))
+      !mul_ok(bd, esize(dt), &bdb) || !mul_ok(bd, 4, &bd4) || !mul_ok(R, 4, &rs) ||
+      rd > (INT64_MAX >> 8))
     return ADALN_ERR_UNSUPPORTED_SHAPE;
   s->R = R;
   s->row_bytes_total = rdb;
   s->mod_bytes = bdb;
   s->stat_bytes = rs;
+  s->sum_bytes_f32 = bd4;
   return ADALN_OK;
 }
 
@@ -124,11 +127,15 @@ adaln_status_t fwd_common(const void* x, const void* shift, const void* scale, f
   return e == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
+// The backward entry points: the fused backward with column sums in the I/O
+// type or in fp32, and the unfused two-pass ablation.
+enum class BwdMode { kFused, kFusedF32Sums, kTwoPass };
+
 adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, const float* mean,
                           const float* rstd, const int64_t* offsets, int64_t B, int64_t N,
                           int64_t R, int64_t D, adaln_dtype_t dtype, void* workspace,
                           size_t workspace_bytes, hipStream_t stream, void* dx, void* dscale,
-                          void* dshift, bool twopass = false) {
+                          void* dshift, BwdMode mode) {
   Sizes s;
   adaln_status_t st = check_shape(B, R, D, dtype, &s);
   if (st != ADALN_OK) return st;
@@ -145,9 +152,11 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
   const int64_t col_blocks = (D + 15) / 16;
   if (wl.tiles_max > INT32_MAX || B > INT32_MAX / col_blocks) return ADALN_ERR_UNSUPPORTED_SHAPE;
 
+  const bool sums_f32 = mode == BwdMode::kFusedF32Sums;
+  const int64_t sum_bytes = sums_f32 ? s.sum_bytes_f32 : s.mod_bytes;
   const Span outs[] = {{dx, s.row_bytes_total},
-                       {dscale, s.mod_bytes},
-                       {dshift, s.mod_bytes},
+                       {dscale, sum_bytes},
+                       {dshift, sum_bytes},
                        {workspace, static_cast<int64_t>(wl.total)}};
   const Span ins[] = {{dy, s.row_bytes_total}, {x, s.row_bytes_total}, {scale, s.mod_bytes},
                       {mean, s.stat_bytes},    {rstd, s.stat_bytes},
@@ -156,6 +165,7 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
 
   const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true, offsets != nullptr);
   const bool vec = vp.ok && aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(scale);
+  const bool twopass = mode == BwdMode::kTwoPass;
   if (twopass && !vec) return ADALN_ERR_UNSUPPORTED_SHAPE;
   char* ws = static_cast<char*>(workspace);
   adaln::Tiling tl{wl.tile_rows, wl.tiles_max, wl.tiles_alloc,
@@ -166,7 +176,7 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
       twopass ? adaln::launch_bwd_twopass(dtype, dy, x, scale, mean, rstd, rm, D, vp, tl, partial,
                                           stream, dx, dscale, dshift)
               : adaln::launch_bwd(dtype, dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial,
-                                  stream, dx, dscale, dshift);
+                                  stream, dx, dscale, dshift, sums_f32);
   return e == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
 }
 
@@ -210,7 +220,7 @@ ADALN_EXPORT adaln_status_t adaln_bwd(const void* dy, const void* x, const void*
   int64_t R;
   if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
   return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
-                    workspace_bytes, stream, dx, dscale, dshift);
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFused);
 }
 
 ADALN_EXPORT adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale,
@@ -222,7 +232,33 @@ ADALN_EXPORT adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, cons
                                              void* dshift) {
   if (!offsets_dev) return ADALN_ERR_INVALID_ARG;
   return bwd_common(dy, x, scale, mean, rstd, offsets_dev, B, 0, total_rows, D, dtype, workspace,
-                    workspace_bytes, stream, dx, dscale, dshift);
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFused);
+}
+
+ADALN_EXPORT adaln_status_t adaln_bwd_f32sums(const void* dy, const void* x, const void* scale,
+                                              const float* mean, const float* rstd, int64_t B,
+                                              int64_t N, int64_t D, adaln_dtype_t dtype,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, void* dx, float* dscale,
+                                              float* dshift) {
+  if (N < 0 || B < 1) return ADALN_ERR_INVALID_ARG;
+  int64_t R;
+  if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
+  return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFusedF32Sums);
+}
+
+ADALN_EXPORT adaln_status_t adaln_bwd_varlen_f32sums(const void* dy, const void* x,
+                                                     const void* scale, const float* mean,
+                                                     const float* rstd,
+                                                     const int64_t* offsets_dev, int64_t B,
+                                                     int64_t total_rows, int64_t D,
+                                                     adaln_dtype_t dtype, void* workspace,
+                                                     size_t workspace_bytes, hipStream_t stream,
+                                                     void* dx, float* dscale, float* dshift) {
+  if (!offsets_dev) return ADALN_ERR_INVALID_ARG;
+  return bwd_common(dy, x, scale, mean, rstd, offsets_dev, B, 0, total_rows, D, dtype, workspace,
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFusedF32Sums);
 }
 
 ADALN_EXPORT adaln_status_t adaln_bwd_twopass(const void* dy, const void* x, const void* scale,
@@ -235,7 +271,7 @@ ADALN_EXPORT adaln_status_t adaln_bwd_twopass(const void* dy, const void* x, con
   int64_t R;
   if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
   return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
-                    workspace_bytes, stream, dx, dscale, dshift, true);
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kTwoPass);
 }
 
 ADALN_EXPORT const char* adaln_status_str(adaln_status_t status) {

@@ -83,10 +83,11 @@ hipError_t launch_fwd(int dtype, const void* x, const void* shift, const void* s
                       const RowMap& rm, int64_t D, bool vec, const VecPlan& vp, int num_cu,
                       hipStream_t stream, void* y, float* mean, float* rstd);
 
+// sums_f32: dscale and dshift are fp32 whatever dtype is (else dtype).
 hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scale,
                       const float* mean, const float* rstd, const RowMap& rm, int64_t D,
                       bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
-                      hipStream_t stream, void* dx, void* dscale, void* dshift);
+                      hipStream_t stream, void* dx, void* dscale, void* dshift, bool sums_f32);
 
 // The two-pass backward: dx rows, then D-tile column partials that read dy
 // and x again, then the finish.  Vectorised plans only (vp.ok, 16-byte

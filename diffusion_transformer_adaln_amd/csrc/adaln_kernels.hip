@@ -69,6 +69,10 @@ template <> struct Elem<F32> {
   __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
     static_cast<float*>(p)[i] = v;
   }
+  // an fp64 sum stored with one rounding (to nearest, ties to even)
+  __device__ static __forceinline__ void store_sum(void* p, int64_t i, double v) {
+    static_cast<float*>(p)[i] = static_cast<float>(v);
+  }
   // acc + the sum of the vector's elements
   __device__ static __forceinline__ float accumulate(const uint4& v, float acc) {
     return acc + __uint_as_float(v.x) + __uint_as_float(v.y) + __uint_as_float(v.z) +
@@ -101,6 +105,24 @@ template <> struct Elem<BF16> {
   }
   __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
     static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+  }
+  // An fp64 sum stored with one rounding to bf16 (to nearest, ties to even).
+  // Rounding to fp32 first and then to bf16 could land a value just off a
+  // bf16 midpoint exactly on it and break the tie the wrong way, so the
+  // fp32 step rounds to odd instead: v itself if it is an fp32 value, else
+  // whichever of the two fp32 values around v has an odd significand.  With
+  // 24 >= 8 + 2 significand bits, round-to-odd followed by
+  // round-to-nearest-even gives the correctly rounded result (Boldo and
+  // Melquiond, "Emulation of FMA and correctly rounded sums: proved
+  // algorithms using rounding to odd", IEEE TC 2008).  The nearest fp32
+  // value t is one of the two; when it is even, its neighbour towards v (one
+  // step in the bit pattern, whose parity alternates) is the odd one.
+  __device__ static __forceinline__ void store_sum(void* p, int64_t i, double v) {
+    const float t = static_cast<float>(v);
+    const double back = static_cast<double>(t);
+    uint32_t b = __float_as_uint(t);
+    if (back != v && !(b & 1u)) b = fabs(v) > fabs(back) ? b + 1u : b - 1u;
+    store1(p, i, __uint_as_float(b));
   }
   // acc + the sum of the vector's elements: one v_dot2_f32_bf16 against
   // (1, 1) per packed pair, straight from the stored bits (the products are
@@ -928,7 +950,10 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
 // ---------------------------------------------------------------------------
 // Both variants add the tiles in an order fixed by the shape and the CU count
-// alone, in fp64, and round once to the output type: bitwise repeatable, no
+// alone, in fp64 (the narrow one rounds its per-slice sums of at most 8 tiles
+// to fp32 on the way through LDS), and round the result once to the output
+// type, which is the template's DT: the I/O type, or F32 for callers that
+// want fp32 column sums whatever the I/O type.  Bitwise repeatable, no
 // atomics.  Measured alternatives on MI355X (video shape) and why they lost:
 // one thread walking all tiles of its column (49 us, latency-bound); a
 // cooperative grid sync (about 30 us per sync); a last-arriving-workgroup
@@ -969,8 +994,12 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   constexpr int RUNS = NSLICE / 8;
   __shared__ float4 sl_h[NSLICE][LANES];    // per-slice sums (fp32: at most PER tiles each)
   __shared__ float4 sl_s[NSLICE][LANES];
-  __shared__ double run_h[4][RUNS][LANES];  // component-major: a wave's stores are contiguous
-  __shared__ double run_s[4][RUNS][LANES];
+  // component-major, so a wave's stores are contiguous; each component's
+  // plane is padded by 4 doubles so that the 32 threads of the last step,
+  // one per (component, quantity, lane), read distinct banks
+  constexpr int RUN_PLANE = RUNS * LANES + 4;
+  __shared__ double run_h[4][RUN_PLANE];
+  __shared__ double run_s[4][RUN_PLANE];
   const int64_t b = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - static_cast<int>(b * col_blocks);
   const int lane = threadIdx.x % LANES;
@@ -1013,18 +1042,21 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
       c[0] += y.x; c[1] += y.y; c[2] += y.z; c[3] += y.w;
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) { run_h[w][slice][lane] = a[w]; run_s[w][slice][lane] = c[w]; }
+    for (int w = 0; w < 4; ++w) {
+      run_h[w][slice * LANES + lane] = a[w];
+      run_s[w][slice * LANES + lane] = c[w];
+    }
   }
   __syncthreads();
-  if (slice == 0 && col_ok) {
+  // one output per thread: slices 0-3 add component `slice` of the shift
+  // sums, slices 4-7 that of the scale sums, the runs in run order
+  if (slice < 8 && col_ok) {
+    const int w = slice & 3;
+    const double* run = slice < 4 ? run_h[w] : run_s[w];
+    double a = 0.0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      double a = 0.0, c = 0.0;
-#pragma unroll
-      for (int q = 0; q < RUNS; ++q) { a += run_h[w][q][lane]; c += run_s[w][q][lane]; }
-      E::store1(dshift, b * D + d + w, static_cast<float>(a));
-      E::store1(dscale, b * D + d + w, static_cast<float>(c));
-    }
+    for (int q = 0; q < RUNS; ++q) a += run[q * LANES + lane];
+    E::store_sum(slice < 4 ? dshift : dscale, b * D + d + w, a);
   }
 }
 
@@ -1072,11 +1104,13 @@ finish_tiles_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int
   sh_h[slice][lane] = h;
   sh_s[slice][lane] = s;
   __syncthreads();
-  if (slice == 0 && d < D) {
+  // slice 0 finishes the shift sums, slice 1 the scale sums
+  if (slice < 2 && d < D) {
+    const double (*sh)[TILES_COLS] = slice == 0 ? sh_h : sh_s;
+    double v = sh[0][lane];
 #pragma unroll
-    for (int k = 1; k < TILES_SLICES; ++k) { h += sh_h[k][lane]; s += sh_s[k][lane]; }
-    E::store1(dshift, b * D + d, static_cast<float>(h));
-    E::store1(dscale, b * D + d, static_cast<float>(s));
+    for (int k = 1; k < TILES_SLICES; ++k) v += sh[k][lane];
+    E::store_sum(slice == 0 ? dshift : dscale, b * D + d, v);
   }
 }
 
@@ -1253,7 +1287,8 @@ template <int DT>
 static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
                                const float* mean, const float* rstd, const RowMap& rm, int64_t D,
                                bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
-                               hipStream_t stream, void* dx, void* dscale, void* dshift) {
+                               hipStream_t stream, void* dx, void* dscale, void* dshift,
+                               bool sums_f32) {
   hipError_t e = hipSuccess;
   if (rm.offsets != nullptr) {
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
@@ -1277,7 +1312,8 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
     }
     if (e != hipSuccess) return e;
   }
-  return finish_launch<DT>(rm, D, tl, partial, stream, dscale, dshift);
+  return sums_f32 ? finish_launch<F32>(rm, D, tl, partial, stream, dscale, dshift)
+                  : finish_launch<DT>(rm, D, tl, partial, stream, dscale, dshift);
 }
 
 // finish: the narrow kernel for few samples whose tiles fit one workgroup,
@@ -1357,10 +1393,10 @@ hipError_t launch_bwd_twopass(int dtype, const void* dy, const void* x, const vo
 hipError_t launch_bwd(int dtype, const void* dy, const void* x, const void* scale,
                       const float* mean, const float* rstd, const RowMap& rm, int64_t D,
                       bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
-                      hipStream_t stream, void* dx, void* dscale, void* dshift) {
+                      hipStream_t stream, void* dx, void* dscale, void* dshift, bool sums_f32) {
   return dtype == BF16
-             ? bwd_dispatch<BF16>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift)
-             : bwd_dispatch<F32>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift);
+             ? bwd_dispatch<BF16>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift, sums_f32)
+             : bwd_dispatch<F32>(dy, x, scale, mean, rstd, rm, D, vec, vp, tl, partial, stream, dx, dscale, dshift, sums_f32);
 }
 
 }  // namespace adaln

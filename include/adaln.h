@@ -26,8 +26,10 @@
  * x, y, dy, dx are [R, D] (R token rows; a dense batch is [B, N, D] with
  * R = B*N); shift, scale, dscale, dshift are [B, D]; mean and rstd are fp32
  * [R].  x, y, dy, dx, shift, scale, dscale, dshift all have the element type
- * `dtype`; statistics and every accumulation are fp32; bf16 results are
- * rounded to nearest, ties to even, once.
+ * `dtype` (except the *_f32sums backward entry points, whose dscale and
+ * dshift are fp32); statistics and every accumulation are fp32 (the column
+ * sums are finished in fp64); every result is rounded to its output type
+ * (to nearest, ties to even) once.
  *
  * Ownership.  Every pointer is a device pointer owned by the caller; the
  * library never allocates, frees or synchronises, and keeps no state except
@@ -65,7 +67,8 @@
 extern "C" {
 #endif
 
-#define ADALN_ABI_VERSION 1
+/* 2: adds adaln_bwd_f32sums and adaln_bwd_varlen_f32sums */
+#define ADALN_ABI_VERSION 2
 
 /* Element type of x, y, dy, dx, shift, scale, dscale, dshift. */
 typedef enum {
@@ -173,6 +176,40 @@ adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale
                                 int64_t D, adaln_dtype_t dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 void* dx, void* dscale, void* dshift);
+
+/*
+ * adaln_bwd_f32sums, adaln_bwd_varlen_f32sums -- adaln_bwd and
+ * adaln_bwd_varlen with dscale and dshift returned in fp32 whatever `dtype`
+ * is: the same column sums, rounded once from the fp64 finish to fp32
+ * instead of to the I/O type.
+ *
+ *   dscale [B, D]    fp32    sum over the sample's rows of dy * xhat
+ *   dshift [B, D]    fp32    sum over the sample's rows of dy
+ *
+ * For callers that add these sums to others before rounding: a sequence
+ * split over devices, where each device holds the sums over its own rows
+ * and the shares are added across devices (the column sums are the only
+ * part of the operator that spans rows; section 2.B, backward bullet), or
+ * gradient accumulation in fp32 over micro-batches.  dx is
+ * bitwise identical to adaln_bwd's / adaln_bwd_varlen's; with dtype ==
+ * ADALN_F32 the whole result is.  Every other argument, the workspace (the
+ * size adaln_bwd_workspace_size reports), launches and errors as in
+ * adaln_bwd / adaln_bwd_varlen; aliasing is checked with dscale and dshift
+ * as 4*B*D-byte buffers.
+ */
+adaln_status_t adaln_bwd_f32sums(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd,
+                                 int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 void* dx, float* dscale, float* dshift);
+
+adaln_status_t adaln_bwd_varlen_f32sums(const void* dy, const void* x, const void* scale,
+                                        const float* mean, const float* rstd,
+                                        const int64_t* offsets_dev, int64_t B,
+                                        int64_t total_rows, int64_t D, adaln_dtype_t dtype,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream, void* dx, float* dscale,
+                                        float* dshift);
 
 /*
  * adaln_bwd_twopass -- the same backward as adaln_bwd, computed the way the

@@ -6,7 +6,8 @@
 //
 // Checks, for every entry point: each documented error code is returned for
 // its cause, a failing call launches nothing, a valid call launches exactly
-// once with the shape it was given, adaln_bwd_workspace_size() is enough for
+// once with the shape (and, for the backward, the column-sum type) it was
+// given, fp32 column sums are sized as such for the aliasing check, adaln_bwd_workspace_size() is enough for
 // both backward entry points, and each of them accepts exactly its own
 // workspace layout and rejects one byte less.  Also the host planner's
 // invariants that the kernels rely on (row layouts for every D, tilings).
@@ -29,6 +30,7 @@ static int g_launches = 0;
 static adaln::RowMap g_rm{};
 static int64_t g_D = 0;
 static adaln::Tiling g_tl{};
+static bool g_sums_f32 = false;
 
 hipError_t hipGetDevice(int* dev) {
   *dev = 0;
@@ -48,8 +50,8 @@ hipError_t launch_fwd(int, const void*, const void*, const void*, float, const R
 }
 hipError_t launch_bwd(int, const void*, const void*, const void*, const float*, const float*,
                       const RowMap& rm, int64_t D, bool, const VecPlan&, const Tiling& tl, float*,
-                      hipStream_t, void*, void*, void*) {
-  ++g_launches; g_rm = rm; g_D = D; g_tl = tl;
+                      hipStream_t, void*, void*, void*, bool sums_f32) {
+  ++g_launches; g_rm = rm; g_D = D; g_tl = tl; g_sums_f32 = sums_f32;
   return hipSuccess;
 }
 hipError_t launch_bwd_twopass(int, const void*, const void*, const void*, const float*,
@@ -202,6 +204,34 @@ static void test_backward() {
   // N == 0: the backward still runs (its finish writes zero dscale/dshift)
   ACCEPT(1, adaln_bwd(nullptr, nullptr, sc, nullptr, nullptr, B, 0, D, bf, ws, adaln_bwd_workspace_size(B, 0, D, bf),
                       nullptr, nullptr, dsc, dsh));
+
+  // fp32 column sums: the same checks, the flag reaches the launcher, and the
+  // sums are 4*B*D-byte buffers for the aliasing check whatever dtype is
+  float *fsc = fat(5), *fsh = fat(6);
+  ACCEPT(1, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, fsc, fsh));
+  EXPECT(g_sums_f32 && g_rm.R == B * N && g_rm.offsets == nullptr && g_D == D,
+         "f32-sums backward launched with the wrong shape or flag");
+  ACCEPT(1, adaln_bwd(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, dsc, dsh));
+  EXPECT(!g_sums_f32, "adaln_bwd launched with fp32 sums");
+  float* after_bf16 = reinterpret_cast<float*>(static_cast<char*>(dsc) + B * D * 2);   // inside fp32 dscale
+  ACCEPT(1, adaln_bwd(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, dsc, after_bf16));
+  REJECT(ADALN_ERR_ALIASING, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, fsc, after_bf16));
+  ACCEPT(1, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, fsc, fsc + B * D));
+  REJECT(ADALN_ERR_ALIASING, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, fsc,
+                                               fsc + B * D - 1));
+  REJECT(ADALN_ERR_ALIASING, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx,
+                                               static_cast<float*>(sc), fsh));
+  REJECT(ADALN_ERR_WORKSPACE_TOO_SMALL, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws,
+                                                          adaln::bwd_workspace_layout(B, B * N, D, 256, false, N).total - 1,
+                                                          nullptr, dx, fsc, fsh));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, bf, ws, need, nullptr, dx, nullptr, fsh));
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_bwd_f32sums(dy, x, sc, m, r, B, -1, D, bf, ws, need, nullptr, dx, fsc, fsh));
+  REJECT(ADALN_ERR_UNSUPPORTED_DTYPE, adaln_bwd_f32sums(dy, x, sc, m, r, B, N, D, (adaln_dtype_t)3, ws, need,
+                                                        nullptr, dx, fsc, fsh));
+  REJECT(ADALN_ERR_UNSUPPORTED_SHAPE, adaln_bwd_f32sums(dy, x, sc, m, r, INT64_MAX / 8, 1, 4096, bf, ws, need,
+                                                        nullptr, dx, fsc, fsh));
+  ACCEPT(1, adaln_bwd_f32sums(nullptr, nullptr, sc, nullptr, nullptr, B, 0, D, ADALN_F32, ws,
+                              adaln_bwd_workspace_size(B, 0, D, ADALN_F32), nullptr, nullptr, fsc, fsh));
   // workspace query: invalid sizes give 0
   EXPECT(adaln_bwd_workspace_size(0, 10, D, bf) == 0, "B = 0 accepted by the size query");
   EXPECT(adaln_bwd_workspace_size(B, -1, D, bf) == 0, "negative rows accepted by the size query");
@@ -231,6 +261,23 @@ static void test_backward_varlen() {
     }
   }
   REJECT(ADALN_ERR_INVALID_ARG, adaln_bwd_varlen(dy, x, sc, m, r, nullptr, 2, 10, 64, bf, ws, 1 << 20, nullptr, dx, dsc, dsh));
+
+  // fp32 column sums of packed samples
+  float *fsc = fat(5), *fsh = fat(6);
+  const int64_t B = 277, R = 229368, D = 3072;
+  const size_t need = adaln_bwd_workspace_size(B, R, D, bf);
+  ACCEPT(1, adaln_bwd_varlen_f32sums(dy, x, sc, m, r, off, B, R, D, bf, ws, need, nullptr, dx, fsc, fsh));
+  EXPECT(g_sums_f32 && g_rm.offsets == off && g_tl.tile_start != nullptr && g_rm.R == R,
+         "packed f32-sums backward launched with the wrong shape or flag");
+  REJECT(ADALN_ERR_INVALID_ARG, adaln_bwd_varlen_f32sums(dy, x, sc, m, r, nullptr, B, R, D, bf, ws, need, nullptr,
+                                                         dx, fsc, fsh));
+  REJECT(ADALN_ERR_ALIASING, adaln_bwd_varlen_f32sums(dy, x, sc, m, r, off, B, R, D, bf, ws, need, nullptr, dx, fsc,
+                                                      fsc + B * D - 4));
+  REJECT(ADALN_ERR_ALIASING, adaln_bwd_varlen_f32sums(dy, x, sc, m, r, off, B, R, D, bf, ws, need, nullptr, dx, fsc,
+                                                      reinterpret_cast<float*>(const_cast<int64_t*>(off))));
+  REJECT(ADALN_ERR_WORKSPACE_TOO_SMALL,
+         adaln_bwd_varlen_f32sums(dy, x, sc, m, r, off, B, R, D, bf, ws,
+                                  adaln::bwd_workspace_layout(B, R, D, 256, true, 0).total - 1, nullptr, dx, fsc, fsh));
 }
 
 static void test_status_strings() {

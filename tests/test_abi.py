@@ -20,7 +20,7 @@ def declared_functions():
     names = set()
     for path in HEADERS:
         src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
-        names |= set(re.findall(r"\b(adaln_[a-z_]+)\s*\(", src))
+        names |= set(re.findall(r"\b(adaln_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
 
 
@@ -42,7 +42,7 @@ def test_header_matches_binding_and_exports(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.adaln_abi_version() == 1
+    assert lib.adaln_abi_version() == 2
     for code, name in adaln._lib.STATUS_NAMES.items():
         assert adaln.adaln_status_str(code) == name
     assert adaln.adaln_status_str(99) == "ADALN_ERR_UNKNOWN"

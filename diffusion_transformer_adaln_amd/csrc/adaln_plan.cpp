@@ -29,8 +29,8 @@ size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
 constexpr int BWD_TILES_PER_CU = 2;
 // Packed batches mix short and long samples, so their tiles vary in length;
 // four tiles per CU lets the workgroup dispatcher even out the load (mixed
-// 256..32760-row samples at D = 3072: 952 us at two per CU, 907 at four, 927
-// at eight).
+// 256..32760-row samples at D = 3072, backward call: 946 us at two per CU,
+// 914 at three, 862 at four, 899 at six, 872 at eight).
 constexpr int BWD_VARLEN_TILES_PER_CU = 4;
 
 // Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,

@@ -23,9 +23,10 @@ size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
 }
 
 // Backward tiles per compute unit for dense batches: a tile's column partials
-// cost 8*D bytes written and read again, so fewer, longer tiles are cheaper;
-// two per CU measured best on the video shape (one: 150 us, three: 159 us,
-// two: 107 us).
+// cost 8*D bytes written and read again, so fewer, longer tiles are cheaper,
+// but a CU needs enough rows in flight.  Two per CU measured best (backward
+// call, video shape: one 147 us, two 102, three 128, four 142; MMDiT 42.9,
+// 37.9, 42.8, 44.1; DiT 24.2, 20.9, 26.1, 24.7).
 constexpr int BWD_TILES_PER_CU = 2;
 // Packed batches mix short and long samples, so their tiles vary in length;
 // four tiles per CU lets the workgroup dispatcher even out the load (mixed

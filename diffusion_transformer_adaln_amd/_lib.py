@@ -123,6 +123,23 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _expect(t, shape, dtype, name):
+    """A tensor the library reads or writes as `shape` elements of `dtype`:
+    anything else would make it read or write past the tensor's storage."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _expect_stats(t, n, name):
+    """mean / rstd: float32 with n elements (any shape, e.g. [B, N] or [R])."""
+    if t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+
+
 def _check_dev(*ts):
     """Index of the one GPU all given tensors live on; they must be contiguous."""
     dev = None
@@ -199,6 +216,9 @@ def adaln_fwd(x, shift, scale, eps: float, y=None, mean=None, rstd=None, stream=
     y = torch.empty_like(x) if y is None else y
     mean = torch.empty((B, N), dtype=torch.float32, device=x.device) if mean is None else mean
     rstd = torch.empty((B, N), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _expect(y, x.shape, x.dtype, "y")
+    _expect_stats(mean, B * N, "mean")
+    _expect_stats(rstd, B * N, "rstd")
     dev = _check_dev(x, shift, scale, y, mean, rstd)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd, _ptr(x), _ptr(shift), _ptr(scale), float(eps), B, N, D,
@@ -217,9 +237,14 @@ def adaln_fwd_varlen(x, shift, scale, offsets, eps: float, y=None, mean=None, rs
         raise ValueError("shift/scale must be [B, D] and offsets [B+1]")
     if offsets.dtype != torch.int64:
         raise TypeError("offsets must be int64")
+    if not (x.dtype == shift.dtype == scale.dtype):
+        raise TypeError("x, shift and scale must share a dtype")
     y = torch.empty_like(x) if y is None else y
     mean = torch.empty((R,), dtype=torch.float32, device=x.device) if mean is None else mean
     rstd = torch.empty((R,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _expect(y, x.shape, x.dtype, "y")
+    _expect_stats(mean, R, "mean")
+    _expect_stats(rstd, R, "rstd")
     dev = _check_dev(x, shift, scale, offsets, y, mean, rstd)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd_varlen, _ptr(x), _ptr(shift), _ptr(scale), float(eps), _ptr(offsets),
@@ -266,9 +291,14 @@ def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stre
     dx = torch.empty_like(x) if dx is None else dx
     dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
     dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
+    _expect(dy, x.shape, x.dtype, "dy")
+    _expect(scale, (B, D), x.dtype, "scale")
+    _expect_stats(mean, B * N, "mean")
+    _expect_stats(rstd, B * N, "rstd")
+    _expect(dx, x.shape, x.dtype, "dx")
+    _expect(dscale, (B, D), sums_dtype, "dscale")
+    _expect(dshift, (B, D), sums_dtype, "dshift")
     dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
-    if mean.dtype != torch.float32 or rstd.dtype != torch.float32:
-        raise TypeError("mean and rstd must be float32")
     lib = load_library()
     workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace)
     st = _on(dev, getattr(lib, fn), _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
@@ -304,6 +334,13 @@ def _bwd_varlen(fn, dy, x, scale, mean, rstd, offsets, workspace, dx, dscale, ds
     dx = torch.empty_like(x) if dx is None else dx
     dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
     dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
+    _expect(dy, x.shape, x.dtype, "dy")
+    _expect(scale, (B, D), x.dtype, "scale")
+    _expect_stats(mean, R, "mean")
+    _expect_stats(rstd, R, "rstd")
+    _expect(dx, x.shape, x.dtype, "dx")
+    _expect(dscale, (B, D), sums_dtype, "dscale")
+    _expect(dshift, (B, D), sums_dtype, "dshift")
     dev = _check_dev(dy, x, scale, mean, rstd, offsets, dx, dscale, dshift)
     lib = load_library()
     workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace)

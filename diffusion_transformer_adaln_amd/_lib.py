@@ -125,19 +125,21 @@ def _ptr(t):
 
 def _expect(t, shape, dtype, name):
     """A tensor the library reads or writes as `shape` elements of `dtype`:
-    anything else would make it read or write past the tensor's storage."""
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    if t.dtype != dtype:
+    anything else would make it read or write past the tensor's storage.
+    (`shape` is a tuple or torch.Size; the check costs well under a
+    microsecond, which matters for the small workloads' per-call cost.)"""
+    if t.dtype is not dtype or t.shape != shape:
+        if t.shape != shape:
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 def _expect_stats(t, n, name):
     """mean / rstd: float32 with n elements (any shape, e.g. [B, N] or [R])."""
+    if t.dtype is not torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
     if t.numel() != n:
         raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name} must be float32, got {t.dtype}")
 
 
 def _check_dev(*ts):
@@ -213,12 +215,19 @@ def adaln_fwd(x, shift, scale, eps: float, y=None, mean=None, rstd=None, stream=
         raise ValueError("shift and scale must be [B, D]")
     if not (x.dtype == shift.dtype == scale.dtype):
         raise TypeError("x, shift and scale must share a dtype")
-    y = torch.empty_like(x) if y is None else y
-    mean = torch.empty((B, N), dtype=torch.float32, device=x.device) if mean is None else mean
-    rstd = torch.empty((B, N), dtype=torch.float32, device=x.device) if rstd is None else rstd
-    _expect(y, x.shape, x.dtype, "y")
-    _expect_stats(mean, B * N, "mean")
-    _expect_stats(rstd, B * N, "rstd")
+    # caller-supplied outputs are checked; the ones made here are right by construction
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _expect(y, x.shape, x.dtype, "y")
+    if mean is None:
+        mean = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    else:
+        _expect_stats(mean, B * N, "mean")
+    if rstd is None:
+        rstd = torch.empty((B, N), dtype=torch.float32, device=x.device)
+    else:
+        _expect_stats(rstd, B * N, "rstd")
     dev = _check_dev(x, shift, scale, y, mean, rstd)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd, _ptr(x), _ptr(shift), _ptr(scale), float(eps), B, N, D,
@@ -239,12 +248,18 @@ def adaln_fwd_varlen(x, shift, scale, offsets, eps: float, y=None, mean=None, rs
         raise TypeError("offsets must be int64")
     if not (x.dtype == shift.dtype == scale.dtype):
         raise TypeError("x, shift and scale must share a dtype")
-    y = torch.empty_like(x) if y is None else y
-    mean = torch.empty((R,), dtype=torch.float32, device=x.device) if mean is None else mean
-    rstd = torch.empty((R,), dtype=torch.float32, device=x.device) if rstd is None else rstd
-    _expect(y, x.shape, x.dtype, "y")
-    _expect_stats(mean, R, "mean")
-    _expect_stats(rstd, R, "rstd")
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _expect(y, x.shape, x.dtype, "y")
+    if mean is None:
+        mean = torch.empty((R,), dtype=torch.float32, device=x.device)
+    else:
+        _expect_stats(mean, R, "mean")
+    if rstd is None:
+        rstd = torch.empty((R,), dtype=torch.float32, device=x.device)
+    else:
+        _expect_stats(rstd, R, "rstd")
     dev = _check_dev(x, shift, scale, offsets, y, mean, rstd)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd_varlen, _ptr(x), _ptr(shift), _ptr(scale), float(eps), _ptr(offsets),
@@ -283,21 +298,34 @@ def adaln_bwd_twopass(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=
     return _bwd_dense("adaln_bwd_twopass", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
 
 
+def _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift):
+    """The backward's outputs: the caller's, checked, else new ones."""
+    if dx is None:
+        dx = torch.empty_like(x)
+    else:
+        _expect(dx, x.shape, x.dtype, "dx")
+    if dscale is None:
+        dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device)
+    else:
+        _expect(dscale, (B, D), sums_dtype, "dscale")
+    if dshift is None:
+        dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device)
+    else:
+        _expect(dshift, (B, D), sums_dtype, "dshift")
+    return dx, dscale, dshift
+
+
 def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream, sums_dtype=None):
     if x.dim() != 3 or dy.shape != x.shape:
         raise ValueError(f"{fn} expects dy and x of shape [B, N, D]")
     B, N, D = x.shape
     sums_dtype = x.dtype if sums_dtype is None else sums_dtype
-    dx = torch.empty_like(x) if dx is None else dx
-    dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
-    dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
-    _expect(dy, x.shape, x.dtype, "dy")
+    if dy.dtype is not x.dtype:
+        raise TypeError(f"dy must be {x.dtype}, got {dy.dtype}")
     _expect(scale, (B, D), x.dtype, "scale")
     _expect_stats(mean, B * N, "mean")
     _expect_stats(rstd, B * N, "rstd")
-    _expect(dx, x.shape, x.dtype, "dx")
-    _expect(dscale, (B, D), sums_dtype, "dscale")
-    _expect(dshift, (B, D), sums_dtype, "dshift")
+    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift)
     dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
     lib = load_library()
     workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace)
@@ -331,16 +359,12 @@ def _bwd_varlen(fn, dy, x, scale, mean, rstd, offsets, workspace, dx, dscale, ds
     if offsets.shape != (B + 1,) or offsets.dtype != torch.int64:
         raise ValueError("offsets must be int64 [B+1]")
     sums_dtype = x.dtype if sums_dtype is None else sums_dtype
-    dx = torch.empty_like(x) if dx is None else dx
-    dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dscale is None else dscale
-    dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device) if dshift is None else dshift
-    _expect(dy, x.shape, x.dtype, "dy")
+    if dy.dtype is not x.dtype:
+        raise TypeError(f"dy must be {x.dtype}, got {dy.dtype}")
     _expect(scale, (B, D), x.dtype, "scale")
     _expect_stats(mean, R, "mean")
     _expect_stats(rstd, R, "rstd")
-    _expect(dx, x.shape, x.dtype, "dx")
-    _expect(dscale, (B, D), sums_dtype, "dscale")
-    _expect(dshift, (B, D), sums_dtype, "dshift")
+    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift)
     dev = _check_dev(dy, x, scale, mean, rstd, offsets, dx, dscale, dshift)
     lib = load_library()
     workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace)

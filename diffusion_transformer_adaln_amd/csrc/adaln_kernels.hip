@@ -32,9 +32,11 @@
 //   * The backward keeps each lane's column partial sums of dy and dy*xhat in
 //     registers over a tile of rows inside one sample, combines the slots of a
 //     workgroup through LDS in slot order, and writes them once per tile,
-//     coalesced along D.  A finish kernel adds a sample's tiles in an order
-//     fixed by the shape and the CU count.  No floating-point atomics
-//     anywhere: bitwise repeatable.
+//     coalesced along D.  A finish kernel adds a sample's tiles in fp64, in
+//     an order fixed by the shape and the CU count, and rounds each sum once
+//     to the output type (the I/O type, or fp32 when the caller asks for
+//     fp32 column sums).  No floating-point atomics anywhere: bitwise
+//     repeatable.
 //
 // General kernels (any D, any alignment) cover the shapes the vector layout
 // cannot; they compute the same quantities with scalar accesses.

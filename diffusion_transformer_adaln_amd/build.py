@@ -69,5 +69,31 @@ def build(verbose: bool = False, out: str = LIB_PATH) -> str:
     return out
 
 
+# A torch-free C consumer of the ABI, run by a GPU test (tests/c/adaln_c_check.c).
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c", "adaln_c_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c", "adaln_c_check")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile the C consumer against the built library (host code only, with
+    the system C compiler); returns the executable's path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for tests/c/adaln_c_check.c")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(ROCM, "include"),
+           C_CHECK_SRC, "-o", C_CHECK_BIN,
+           "-L" + HERE, "-ladaln", "-Wl,-rpath,$ORIGIN/../../diffusion_transformer_adaln_amd",
+           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"C consumer build failed ({proc.returncode}):\n{proc.stdout}{proc.stderr}")
+    return C_CHECK_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_check(verbose="-v" in sys.argv))

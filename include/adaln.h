@@ -110,9 +110,10 @@ adaln_status_t adaln_fwd(const void* x, const void* shift, const void* scale, fl
                          hipStream_t stream, void* y, float* mean, float* rstd);
 
 /*
- * adaln_bwd_workspace_size -- bytes of device workspace adaln_bwd and
- * adaln_bwd_varlen need for B samples, total_rows rows and D features on the
- * current device.  Returns 0 for invalid sizes.  The size depends on the
+ * adaln_bwd_workspace_size -- bytes of device workspace every backward entry
+ * point (adaln_bwd, adaln_bwd_varlen, their *_f32sums variants and
+ * adaln_bwd_twopass) needs for B samples, total_rows rows and D features on
+ * the current device.  Returns 0 for invalid sizes.  The size depends on the
  * device's compute-unit count; query it on the device that will run the call.
  */
 size_t adaln_bwd_workspace_size(int64_t B, int64_t total_rows, int64_t D, adaln_dtype_t dtype);

@@ -35,7 +35,9 @@ workload's rows on one host core.
 
 `--bwd twopass` runs the backward through adaln_bwd_twopass instead (dx
 pass, then a separate D-tile column pass that reads dy and x again): the
-same work with more traffic, to measure what the fusion saves.
+same work with more traffic, to measure what the fusion saves.  `--bwd
+f32sums` runs the fp32-column-sum entry points (the same kernels; the byte
+count stays that of the I/O-typed sums, 2*B*D*s fewer bytes than written).
 
 `--cost-sweep` does the shape benchmarking of the batch scheduler instead
 (see cost_sweep) and prints its own JSON line.
@@ -77,9 +79,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "adaln_bwd_video_bf16_traffic.txt"),
                     help="measured HBM bytes per backward call (from rocprofv3 counters), if present")
-    ap.add_argument("--bwd", choices=("fused", "twopass"), default="fused",
-                    help="backward entry point: the fused adaln_bwd, or adaln_bwd_twopass (dx pass, then "
-                         "a separate D-tile column pass that reads dy and x again; dense workloads only)")
+    ap.add_argument("--bwd", choices=("fused", "twopass", "f32sums"), default="fused",
+                    help="backward entry point: the fused adaln_bwd; adaln_bwd_twopass (dx pass, then "
+                         "a separate D-tile column pass that reads dy and x again; dense workloads only); "
+                         "or adaln_bwd_f32sums / adaln_bwd_varlen_f32sums (fp32 column sums)")
     ap.add_argument("--impl", choices=("hip", "torch"), default="hip",
                     help="hip: this library's kernels; torch: the unfused eager-PyTorch chain (dense "
                          "workloads only), for comparison")
@@ -201,8 +204,12 @@ class Runner:
         p = self.p
         if bwd_impl == "twopass" and not p.dense:
             raise SystemExit(f"--bwd twopass takes dense workloads; {p.name} is packed")
-        self.bwd_fn = adaln.adaln_bwd_twopass if bwd_impl == "twopass" else adaln.adaln_bwd
+        self.bwd_fn = {"twopass": adaln.adaln_bwd_twopass,
+                       "f32sums": adaln.adaln_bwd_f32sums}.get(bwd_impl, adaln.adaln_bwd)
+        self.bwd_varlen_fn = (adaln.adaln_bwd_varlen_f32sums if bwd_impl == "f32sums"
+                              else adaln.adaln_bwd_varlen)
         tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+        sdt = torch.float32 if bwd_impl == "f32sums" else tdt      # dscale / dshift
         base = upload(pd)
         S = 4
         per_set = max(1, 4 * p.R * p.D * p.esize)
@@ -217,8 +224,8 @@ class Runner:
                 "y": torch.empty_like(base["x"]), "dx": torch.empty_like(base["x"]),
                 "mean": torch.empty(p.R, dtype=torch.float32, device="cuda"),
                 "rstd": torch.empty(p.R, dtype=torch.float32, device="cuda"),
-                "dscale": torch.empty(p.B, p.D, dtype=tdt, device="cuda"),
-                "dshift": torch.empty(p.B, p.D, dtype=tdt, device="cuda")})
+                "dscale": torch.empty(p.B, p.D, dtype=sdt, device="cuda"),
+                "dshift": torch.empty(p.B, p.D, dtype=sdt, device="cuda")})
         self.ws = torch.empty(max(16, adaln.adaln_bwd_workspace_size(p.B, p.R, p.D, tdt)),
                               dtype=torch.uint8, device="cuda")
         if p.dense:                         # the [B, N, D] / [B, N] views, made once
@@ -237,12 +244,12 @@ class Runner:
                                mean=s["mean"], rstd=s["rstd"])
 
     def bwd(self, s):
-        p, a = self.p, self.adaln
+        p = self.p
         if p.dense:
             self.bwd_fn(s["dy3"], s["x3"], s["scale"], s["mean2"], s["rstd2"], workspace=self.ws,
                         dx=s["dx3"], dscale=s["dscale"], dshift=s["dshift"])
         else:
-            a.adaln_bwd_varlen(s["dy"], s["x"], s["scale"], s["mean"], s["rstd"], s["offsets"],
+            self.bwd_varlen_fn(s["dy"], s["x"], s["scale"], s["mean"], s["rstd"], s["offsets"],
                                workspace=self.ws, dx=s["dx"], dscale=s["dscale"], dshift=s["dshift"])
 
     def prime(self):
@@ -503,7 +510,7 @@ def main():
         torch.cuda.synchronize()
 
     traffic = read_traffic(args.traffic_file, args.config) if (args.bwd, args.impl) == ("fused", "hip") else None
-    bwd_name = "adaln_bwd" if args.bwd == "fused" else "adaln_bwd_twopass"
+    bwd_name = {"fused": "adaln_bwd", "twopass": "adaln_bwd_twopass", "f32sums": "adaln_bwd_f32sums"}[args.bwd]
     if args.impl == "torch":
         bwd_name = "eager PyTorch autograd backward"
 

@@ -511,6 +511,8 @@ def main():
 
     traffic = read_traffic(args.traffic_file, args.config) if (args.bwd, args.impl) == ("fused", "hip") else None
     bwd_name = {"fused": "adaln_bwd", "twopass": "adaln_bwd_twopass", "f32sums": "adaln_bwd_f32sums"}[args.bwd]
+    if not all(pd.problem.dense for pd in pds):      # packed samples go through the varlen entry points
+        bwd_name = bwd_name.replace("adaln_bwd", "adaln_bwd_varlen")
     if args.impl == "torch":
         bwd_name = "eager PyTorch autograd backward"
 

@@ -30,3 +30,13 @@ def test_traffic_is_read_only_for_its_workload_and_sources(tmp_path):
     f.write_text(f"workload: video_bf16\nkernel_source_sha: {'0' * 16}\nbwd_hbm_bytes_per_call: 123\n")
     assert bench.read_traffic(str(f), "video_bf16") is None
     assert bench.read_traffic(str(tmp_path / "missing.txt"), "video_bf16") is None
+
+
+def test_more_than_one_gpu_is_refused_with_a_reason():
+    import subprocess
+    import sys
+
+    run = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert run.returncode != 0
+    assert "exactly one GPU" in run.stdout + run.stderr

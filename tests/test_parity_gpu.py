@@ -106,6 +106,21 @@ def test_shapes(dtype, D, lengths):
         check_all(pd, run_gpu(pd, dense=False))
 
 
+# More samples than the packed backward's one-workgroup prologue scans in one
+# pass (1,024), with empty samples at the pass boundaries, so its carried
+# prefix sum and the many-sample finish are both exercised.
+@pytest.mark.parametrize("dtype,D", [("bf16", 256), ("f32", 128), ("bf16", 3072)])
+def test_many_packed_samples(dtype, D):
+    g = np.random.Generator(np.random.PCG64(17))
+    lengths = g.integers(0, 7, size=2600).tolist()
+    for b in (0, 1023, 1024, 2047, 2048, 2599):
+        lengths[b] = 0
+    lengths[1025] = 40
+    pd = _pd(dtype, D, lengths, seed=18, dense=False)
+    say(f"[many-samples] {dtype} D={D} B={len(lengths)} R={pd.problem.R}")
+    check_all(pd, run_gpu(pd))
+
+
 # The fuzz grid: every D here against one-row, tiny, one-wave-plus and
 # several-thousand-row batches, both dtypes.  The 4,097-row batches are
 # checked on sampled rows and on every sample's full column sums.

@@ -121,6 +121,15 @@ def test_many_packed_samples(dtype, D):
     check_all(pd, run_gpu(pd))
 
 
+# Many short samples through the dense entry points: B far above the narrow
+# finish's 16 samples, tiles of a few rows each.
+@pytest.mark.parametrize("dtype,D,B,N", [("bf16", 1152, 3000, 3), ("f32", 128, 2049, 5)])
+def test_many_dense_samples(dtype, D, B, N):
+    pd = _pd(dtype, D, [N] * B, seed=19, dense=True)
+    say(f"[many-dense] {dtype} D={D} B={B} N={N}")
+    check_all(pd, run_gpu(pd))
+
+
 # The fuzz grid: every D here against one-row, tiny, one-wave-plus and
 # several-thousand-row batches, both dtypes.  The 4,097-row batches are
 # checked on sampled rows and on every sample's full column sums.

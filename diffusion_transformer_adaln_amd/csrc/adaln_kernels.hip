@@ -168,6 +168,18 @@ __device__ __forceinline__ float mul_rounded(float a, float b) {
   return a * b;
 }
 
+// acc / n for a count n: the product with the rounded reciprocal, then one
+// correction step (the residual acc - n*q is exact under an fma).  For a sum
+// of n equal values c (acc = n*c exactly) the result is exactly c, so a row of
+// equal values gets zero variance; a multiply by 1/n alone can miss c by an
+// ulp when 1/n is not an fp32 value (n = 24, 80), and an IEEE division costs
+// a longer dependent chain on the forward's critical path.
+__device__ __forceinline__ float div_count(float acc, float n, float inv_n) {
+  const float q = acc * inv_n;
+  const float r = __builtin_fmaf(-q, n, acc);
+  return __builtin_fmaf(r, inv_n, q);
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane exchange
 // ---------------------------------------------------------------------------
@@ -380,7 +392,7 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
         for (int k = 0; k < EPV; ++k) acc += f[k];
       }
-      const float ml = acc * (1.0f / n_lane);
+      const float ml = div_count(acc, n_lane, 1.0f / n_lane);
       float sq = 0.f;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
@@ -513,7 +525,7 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) acc = E::accumulate(cur[j], acc);
-    const float ml = acc * (1.0f / n_lane);
+    const float ml = div_count(acc, n_lane, 1.0f / n_lane);
     float f[VPT][EPV];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) E::unpack(cur[j], f[j]);

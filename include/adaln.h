@@ -96,7 +96,9 @@ typedef enum {
  *   shift  [B, D]    dtype   per-sample shift
  *   scale  [B, D]    dtype   per-sample scale (rows are multiplied by 1 + scale)
  *   eps              float   added to the biased variance inside the square root;
- *                            finite and >= 0
+ *                            finite and >= 0 (with eps = 0 a row of equal values
+ *                            has no defined normalisation: its rstd is +inf and
+ *                            its y and dx are not finite)
  *   B >= 1, N >= 0, 1 <= D <= ADALN_MAX_D
  *   y      [B*N, D]  dtype   output; must not overlap any input
  *   mean   [B*N]     fp32    saved row means (for adaln_bwd)

@@ -281,6 +281,18 @@ def test_constant_rows(dtype, D):
         # rstd = eps^-1/2 makes |dx| large: outside the workloads' range, where
         # the bf16 format itself sets the error floor
         check_all(pd, run_gpu(pd, eps=eps), eps=eps, strict=False)
+    # eps = 0: a zero-variance row has no defined normalisation; its rstd is
+    # +inf (1/sqrt(0)), as the formula gives in floating point, and the other
+    # rows are untouched by it; dshift (a plain sum of dy) stays finite
+    out = run_gpu(pd, eps=0.0)
+    rstd = out["rstd"].cpu().numpy()
+    assert np.all(np.isposinf(rstd[::3])), rstd[::3]
+    keep = np.ones(pd.problem.R, dtype=bool)
+    keep[::3] = False
+    assert np.all(np.isfinite(rstd[keep]))
+    for k in ("y", "dx"):
+        assert torch.isfinite(out[k][torch.from_numpy(keep).cuda()].float()).all(), k
+    assert torch.isfinite(out["dshift"].float()).all()
 
 
 # Per-row offsets far above the row's spread (|mean|/std up to ~200 in fp32):

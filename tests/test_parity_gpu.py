@@ -281,6 +281,18 @@ def test_constant_rows(dtype, D):
         # rstd = eps^-1/2 makes |dx| large: outside the workloads' range, where
         # the bf16 format itself sets the error floor
         check_all(pd, run_gpu(pd, eps=eps), eps=eps, strict=False)
+    # exactly, for every forward kernel: mean = the value, rstd = 1/sqrt(eps)
+    # (fp32, both steps correctly rounded), y = shift bit for bit
+    eps = 1e-6
+    out = run_gpu(pd, eps=eps)
+    mean = out["mean"].cpu().numpy()[::3]
+    rstd = out["rstd"].cpu().numpy()[::3]
+    assert np.all(mean == np.float32(3.25)), mean
+    assert np.all(rstd == np.float32(1.0) / np.sqrt(np.float32(eps))), rstd
+    bits_t = torch.int16 if dtype == "bf16" else torch.int32
+    y = out["y"][::3].contiguous().view(bits_t).cpu().numpy()
+    want = to_dev(pd.shift, dtype)[0].contiguous().view(bits_t).cpu().numpy()   # one sample
+    assert np.array_equal(y, np.broadcast_to(want, y.shape)), "y of a constant row is not shift"
     # eps = 0: a zero-variance row has no defined normalisation; its rstd is
     # +inf (1/sqrt(0)), as the formula gives in floating point, and the other
     # rows are untouched by it; dshift (a plain sum of dy) stays finite

@@ -3,7 +3,8 @@
 The operator runs in hand-written HIP kernels behind the C ABI declared in
 include/adaln.h; this package holds those sources (csrc/), the build step and
 a ctypes binding whose functions carry the C entry points' names.  The same
-library carries the host-side batch scheduler of include/adaln_sched.h.
+library carries the host-side batch scheduler of include/adaln_sched.h and
+the streaming ceiling probes of include/adaln_probe.h.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -19,6 +20,8 @@ from ._lib import (  # noqa: F401
     adaln_fwd,
     adaln_fwd_varlen,
     adaln_load_cv,
+    adaln_probe_read_out_bytes,
+    adaln_probe_stream,
     adaln_sched_batch_size,
     adaln_sched_plan,
     adaln_status_str,

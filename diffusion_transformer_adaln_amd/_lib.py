@@ -43,6 +43,8 @@ EXPORTED = (
     "adaln_sched_plan",
     "adaln_cost_fit",
     "adaln_load_cv",
+    "adaln_probe_stream",
+    "adaln_probe_read_out_bytes",
 )
 
 
@@ -100,6 +102,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_status_str.restype = ctypes.c_char_p
     lib.adaln_abi_version.argtypes = []
     lib.adaln_abi_version.restype = ctypes.c_int
+    lib.adaln_probe_stream.argtypes = [ctypes.c_int, _P, _P, _P, _I64, ctypes.c_int, ctypes.c_int, _P]
+    lib.adaln_probe_stream.restype = ctypes.c_int
+    lib.adaln_probe_read_out_bytes.argtypes = [ctypes.c_int]
+    lib.adaln_probe_read_out_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -186,6 +192,16 @@ def _raise(fn, st):
         raise AdaLNError(fn, st)
 
 
+def _on_stream(stream, made):
+    """Tensors allocated here come from the caching allocator's pool of the
+    current stream; when the kernels run on another `stream`, record it on
+    them so that their memory is not handed out again before that stream's
+    work on it is done."""
+    if stream is not None:
+        for t in made:
+            t.record_stream(stream)
+
+
 # --------------------------------------------------------------------------
 # public functions (names of the C entry points)
 # --------------------------------------------------------------------------
@@ -216,19 +232,24 @@ def adaln_fwd(x, shift, scale, eps: float, y=None, mean=None, rstd=None, stream=
     if not (x.dtype == shift.dtype == scale.dtype):
         raise TypeError("x, shift and scale must share a dtype")
     # caller-supplied outputs are checked; the ones made here are right by construction
+    made = []
     if y is None:
         y = torch.empty_like(x)
+        made.append(y)
     else:
         _expect(y, x.shape, x.dtype, "y")
     if mean is None:
         mean = torch.empty((B, N), dtype=torch.float32, device=x.device)
+        made.append(mean)
     else:
         _expect_stats(mean, B * N, "mean")
     if rstd is None:
         rstd = torch.empty((B, N), dtype=torch.float32, device=x.device)
+        made.append(rstd)
     else:
         _expect_stats(rstd, B * N, "rstd")
     dev = _check_dev(x, shift, scale, y, mean, rstd)
+    _on_stream(stream, made)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd, _ptr(x), _ptr(shift), _ptr(scale), float(eps), B, N, D,
              _dtype_code(x.dtype), _stream(dev, stream), _ptr(y), _ptr(mean), _ptr(rstd))
@@ -248,19 +269,24 @@ def adaln_fwd_varlen(x, shift, scale, offsets, eps: float, y=None, mean=None, rs
         raise TypeError("offsets must be int64")
     if not (x.dtype == shift.dtype == scale.dtype):
         raise TypeError("x, shift and scale must share a dtype")
+    made = []
     if y is None:
         y = torch.empty_like(x)
+        made.append(y)
     else:
         _expect(y, x.shape, x.dtype, "y")
     if mean is None:
         mean = torch.empty((R,), dtype=torch.float32, device=x.device)
+        made.append(mean)
     else:
         _expect_stats(mean, R, "mean")
     if rstd is None:
         rstd = torch.empty((R,), dtype=torch.float32, device=x.device)
+        made.append(rstd)
     else:
         _expect_stats(rstd, R, "rstd")
     dev = _check_dev(x, shift, scale, offsets, y, mean, rstd)
+    _on_stream(stream, made)
     lib = load_library()
     st = _on(dev, lib.adaln_fwd_varlen, _ptr(x), _ptr(shift), _ptr(scale), float(eps), _ptr(offsets),
              B, R, D, _dtype_code(x.dtype), _stream(dev, stream), _ptr(y), _ptr(mean), _ptr(rstd))
@@ -268,11 +294,13 @@ def adaln_fwd_varlen(x, shift, scale, offsets, eps: float, y=None, mean=None, rs
     return y, mean, rstd
 
 
-def _workspace(B, R, D, dtype, dev, workspace):
-    """A caller's workspace (on device index `dev`), else a new one of the queried size."""
+def _workspace(B, R, D, dtype, dev, workspace, made):
+    """A caller's workspace (on device index `dev`), else a new one of the
+    queried size (appended to `made`)."""
     if workspace is None:
         need = adaln_bwd_workspace_size(B, R, D, dtype, dev)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=torch.device("cuda", dev))
+        made.append(workspace)
     elif _check_dev(workspace) != dev:
         raise ValueError("the workspace must be on the tensors' device")
     return workspace, workspace.numel() * workspace.element_size()
@@ -298,18 +326,22 @@ def adaln_bwd_twopass(dy, x, scale, mean, rstd, workspace=None, dx=None, dscale=
     return _bwd_dense("adaln_bwd_twopass", dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stream)
 
 
-def _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift):
-    """The backward's outputs: the caller's, checked, else new ones."""
+def _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift, made):
+    """The backward's outputs: the caller's, checked, else new ones (appended
+    to `made`)."""
     if dx is None:
         dx = torch.empty_like(x)
+        made.append(dx)
     else:
         _expect(dx, x.shape, x.dtype, "dx")
     if dscale is None:
         dscale = torch.empty((B, D), dtype=sums_dtype, device=x.device)
+        made.append(dscale)
     else:
         _expect(dscale, (B, D), sums_dtype, "dscale")
     if dshift is None:
         dshift = torch.empty((B, D), dtype=sums_dtype, device=x.device)
+        made.append(dshift)
     else:
         _expect(dshift, (B, D), sums_dtype, "dshift")
     return dx, dscale, dshift
@@ -325,10 +357,12 @@ def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stre
     _expect(scale, (B, D), x.dtype, "scale")
     _expect_stats(mean, B * N, "mean")
     _expect_stats(rstd, B * N, "rstd")
-    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift)
+    made = []
+    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift, made)
     dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
     lib = load_library()
-    workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace)
+    workspace, wbytes = _workspace(B, B * N, D, x.dtype, dev, workspace, made)
+    _on_stream(stream, made)
     st = _on(dev, getattr(lib, fn), _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
              _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream), _ptr(dx),
              _ptr(dscale), _ptr(dshift))
@@ -364,10 +398,12 @@ def _bwd_varlen(fn, dy, x, scale, mean, rstd, offsets, workspace, dx, dscale, ds
     _expect(scale, (B, D), x.dtype, "scale")
     _expect_stats(mean, R, "mean")
     _expect_stats(rstd, R, "rstd")
-    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift)
+    made = []
+    dx, dscale, dshift = _bwd_outputs(x, B, D, sums_dtype, dx, dscale, dshift, made)
     dev = _check_dev(dy, x, scale, mean, rstd, offsets, dx, dscale, dshift)
     lib = load_library()
-    workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace)
+    workspace, wbytes = _workspace(B, R, D, x.dtype, dev, workspace, made)
+    _on_stream(stream, made)
     st = _on(dev, getattr(lib, fn), _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd),
              _ptr(offsets), B, R, D, _dtype_code(x.dtype), _ptr(workspace), wbytes,
              _stream(dev, stream), _ptr(dx), _ptr(dscale), _ptr(dshift))
@@ -426,3 +462,39 @@ def adaln_load_cv(loads) -> float:
 
     x = _host(loads, np.float64)
     return float(load_library().adaln_load_cv(x.ctypes.data if x.size else None, x.size))
+
+
+# ---------------------------------------------------------------------------
+# streaming ceiling probes (include/adaln_probe.h)
+# ---------------------------------------------------------------------------
+PROBE_MODES = {"copy": 0, "two_to_one": 1, "read": 2, "write": 3}
+
+
+def adaln_probe_read_out_bytes(wg_per_cu: int, device=None) -> int:
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(lib.adaln_probe_read_out_bytes(int(wg_per_cu)))
+
+
+def adaln_probe_stream(mode: str, a, b, out, wg_per_cu: int, unroll: int, nbytes=None, stream=None):
+    """One streaming pass over uint8 (or any) device tensors: `mode` is one of
+    PROBE_MODES; nbytes defaults to the byte size of `out` (copy, two_to_one,
+    write) or of `a` (read).  Sizes are checked here, since the library cannot
+    see buffer extents."""
+    code = PROBE_MODES[mode]
+    nb = lambda t: t.numel() * t.element_size()
+    if nbytes is None:
+        nbytes = nb(a) if mode == "read" else nb(out)
+    for t, need in ((a, mode != "write"), (b, mode == "two_to_one")):
+        if need and (t is None or nb(t) < nbytes):
+            raise ValueError(f"probe input smaller than {nbytes} bytes")
+    dev = _check_dev(a, b, out)
+    if mode == "read":
+        if nb(out) < adaln_probe_read_out_bytes(wg_per_cu, dev):
+            raise ValueError("read probe output too small")
+    elif nb(out) < nbytes:
+        raise ValueError(f"probe output smaller than {nbytes} bytes")
+    lib = load_library()
+    st = _on(dev, lib.adaln_probe_stream, code, _ptr(a), _ptr(b), _ptr(out), int(nbytes), int(wg_per_cu),
+             int(unroll), _stream(dev, stream))
+    _raise("adaln_probe_stream", st)

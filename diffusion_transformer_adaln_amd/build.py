@@ -4,8 +4,9 @@
 
 Compiles csrc/adaln_api.cpp (host: validation and dispatch),
 csrc/adaln_plan.cpp (host: row layouts, backward tiling, workspace layout),
-csrc/adaln_sched.cpp (host: batch scheduling and cost model) and
-csrc/adaln_kernels.hip (gfx950 kernels) with hipcc into one shared library
+csrc/adaln_sched.cpp (host: batch scheduling and cost model),
+csrc/adaln_kernels.hip (gfx950 kernels) and csrc/adaln_probe.hip (streaming
+ceiling probes, include/adaln_probe.h) with hipcc into one shared library
 next to this file.  Every call recompiles.
 """
 
@@ -23,7 +24,8 @@ LIB_NAME = "libadaln.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = [os.path.join(CSRC, "adaln_api.cpp"), os.path.join(CSRC, "adaln_plan.cpp"),
-           os.path.join(CSRC, "adaln_sched.cpp"), os.path.join(CSRC, "adaln_kernels.hip")]
+           os.path.join(CSRC, "adaln_sched.cpp"), os.path.join(CSRC, "adaln_kernels.hip"),
+           os.path.join(CSRC, "adaln_probe.hip")]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 HIPCC_FLAGS = [

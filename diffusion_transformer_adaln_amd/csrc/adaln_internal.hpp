@@ -22,6 +22,22 @@ struct RowMap {
   const int64_t* offsets;    // device, B+1 entries, or nullptr for dense
 };
 
+// Packed-batch offsets live in device memory and are trusted (the host cannot
+// read them without synchronising), so the kernels clamp every offset they
+// read into [0, R] and treat a sample whose end lies before its start as
+// empty: a malformed table then gives wrong results but no access outside the
+// row tensors (constexpr, so the same function serves the kernels and the
+// host tests).
+constexpr int64_t clamp_row(int64_t v, int64_t R) { return v < 0 ? 0 : (v > R ? R : v); }
+
+// Rows [lo, lo + n) of a packed sample whose offsets are o0 and o1, clamped.
+struct RowSpan {
+  int64_t lo, n;
+};
+constexpr RowSpan clamped_span(int64_t o0, int64_t o1, int64_t R) {
+  return RowSpan{clamp_row(o0, R), clamp_row(o1, R) > clamp_row(o0, R) ? clamp_row(o1, R) - clamp_row(o0, R) : 0};
+}
+
 // Backward tiling: every tile is a run of at most `tile_rows` consecutive rows
 // inside one sample.  Sample b's tiles are numbered
 // [tile_start(b), tile_start(b+1)).  Dense: tile_start(b) = b * ceil(N/tile_rows).

@@ -142,6 +142,16 @@ template <> struct Elem<BF16> {
   }
 };
 
+// x - c for every element of a 16-byte vector, as x + (-c): the same
+// correctly rounded value as the subtraction.
+template <int DT> struct Center {
+  __device__ static __forceinline__ void apply(const uint4& v, float negc, float* d) {
+    Elem<DT>::unpack(v, d);
+#pragma unroll
+    for (int k = 0; k < Elem<DT>::EPV; ++k) d[k] += negc;
+  }
+};
+
 // Streaming (non-temporal) 16-byte accesses for the row tensors of the
 // vectorised kernels: x, dy, y and dx are touched once per call and are far
 // larger than L2 plus the MALL, so caching them buys nothing.  Measured on
@@ -160,13 +170,23 @@ __device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
 }
 
-// Product rounded to fp32 on its own: never fused into a following add, so a
-// value computed twice (once for a row sum, once for the output) has the
-// same bits both times.
-__device__ __forceinline__ float mul_rounded(float a, float b) {
-#pragma clang fp contract(off)
-  return a * b;
-}
+// The backward's per-element arithmetic, shared by every backward kernel so
+// that all of them produce the same bits for the same row:
+//   g  = dy*(1 + scale) with one rounding, as fma(dy, scale, dy);
+//   dx = rstd*((g - a) - xhat*c) with a = sum(g)/D, c = sum(g*xhat)/D.
+// g - a comes first: it is exact when g is close to a, so dx is exactly 0
+// where the formula gives 0 (D = 1, or a constant g on a constant row).
+// Folding rstd in first (rstd*g - rstd*a, two fmas) saves one instruction
+// but leaves the rounding error of rstd*a there instead.
+__device__ __forceinline__ float grad_g(float dy, float scale) { return __builtin_fmaf(dy, scale, dy); }
+struct RowGrad {
+  float rs, a, c;
+  __device__ __forceinline__ RowGrad(float sum_g, float sum_gx, float rstd, float inv_d)
+      : rs(rstd), a(sum_g * inv_d), c(sum_gx * inv_d) {}
+  __device__ __forceinline__ float dx(float g, float xh) const {
+    return rs * __builtin_fmaf(-xh, c, g - a);
+  }
+};
 
 // acc / n for a count n: the product with the rounded reciprocal, then one
 // correction step (the residual acc - n*q is exact under an fma).  For a sum
@@ -250,6 +270,59 @@ __device__ __forceinline__ float sum_unit(float v, int unit) {
   return v;
 }
 
+// The two halves of a cross-row exchange: v_permlane16_swap exchanges the
+// odd 16-lane rows of one register with the even rows of another, and
+// v_permlane32_swap the upper 32 lanes with the lower 32.  Applied to two
+// copies of v, both lanes of a partner pair receive the same ordered pair
+// (value of the lower lane, value of the upper lane), so any function of the
+// pair gives the same bits in both lanes, with no LDS and no lane-index
+// arithmetic.
+struct LanePair {
+  float lower, upper;
+};
+__device__ __forceinline__ LanePair swap16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return LanePair{__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+__device__ __forceinline__ LanePair swap32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return LanePair{__uint_as_float(p[0]), __uint_as_float(p[1])};
+}
+
+// Chan merge of the two halves of a lane pair covering n/2 elements each.
+__device__ __forceinline__ void chan_pair(float& m, float& s, const LanePair& pm, const LanePair& ps,
+                                          float half_n) {
+  const float d = pm.upper - pm.lower;
+  m = 0.5f * (pm.lower + pm.upper);
+  s = (ps.lower + ps.upper) + (d * d) * half_n;
+}
+
+// (mean, M2) over the whole wave, n_lane elements per lane; every lane ends
+// with the same bits.  Four DPP levels inside each 16-lane row, then the
+// row pairs and the half-waves through the swap instructions.
+__device__ __forceinline__ void chan_reduce_wave(float& m, float& s, float n_lane) {
+  float n = n_lane;
+  float mo, so;
+  mo = partner16<0>(m); so = partner16<0>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<1>(m); so = partner16<1>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<2>(m); so = partner16<2>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  mo = partner16<3>(m); so = partner16<3>(s); chan_equal(m, s, mo, so, 0.5f * n); n *= 2.f;
+  chan_pair(m, s, swap16(m), swap16(s), 0.5f * n); n *= 2.f;
+  chan_pair(m, s, swap32(m), swap32(s), 0.5f * n);
+}
+
+// Sum over the whole wave; every lane ends with the same bits.
+__device__ __forceinline__ float sum_wave(float v) {
+  v = v + partner16<0>(v);
+  v = v + partner16<1>(v);
+  v = v + partner16<2>(v);
+  v = v + partner16<3>(v);
+  LanePair p = swap16(v);
+  v = p.lower + p.upper;
+  p = swap32(v);
+  return p.lower + p.upper;
+}
+
 // Lanes that reduce together before LDS: a whole wave when a row covers whole
 // waves, 32 lanes when two rows share a wave, else one 16-lane DPP row.
 __device__ __forceinline__ int reduce_unit(int lpr) {
@@ -261,11 +334,12 @@ __device__ __forceinline__ int reduce_unit(int lpr) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t sample_of_row(const RowMap& rm, int64_t row) {
   if (rm.offsets == nullptr) return row / rm.N;
-  // largest b with offsets[b] <= row  (offsets non-decreasing; empty samples skipped)
+  // largest b with offsets[b] <= row  (offsets non-decreasing; empty samples
+  // skipped); always in [0, B) whatever the table holds
   int64_t lo = 0, hi = rm.B;   // invariant: offsets[lo] <= row < offsets[hi]
   while (hi - lo > 1) {
     const int64_t mid = (lo + hi) >> 1;
-    if (rm.offsets[mid] <= row) lo = mid; else hi = mid;
+    if (clamp_row(rm.offsets[mid], rm.R) <= row) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -295,8 +369,9 @@ __device__ __forceinline__ void tile_rows_of(const RowMap& rm, const Tiling& tl,
     b = lo;
     k = t - tl.tile_start[b];
     tiles = tl.tile_start[b + 1] - tl.tile_start[b];
-    lo_row = rm.offsets[b];
-    n = rm.offsets[b + 1] - lo_row;
+    const RowSpan sp = clamped_span(rm.offsets[b], rm.offsets[b + 1], rm.R);
+    lo_row = sp.lo;
+    n = sp.n;
   }
   if (tl.interleave) {
     first = lo_row + k;
@@ -353,8 +428,8 @@ fwd_vec_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
   int64_t cur_lo = 0, cur_hi = 0;     // rows of the sample whose modulation is loaded
   auto load_mod = [&](int64_t r) {    // unpacked 1 + scale and shift of row r's sample
     const int64_t b = sample_of_row(rm, r);
-    cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
-    cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
+    cur_lo = rm.offsets ? clamp_row(rm.offsets[b], rm.R) : b * rm.N;
+    cur_hi = rm.offsets ? clamp_row(rm.offsets[b + 1], rm.R) : cur_lo + rm.N;
     const uint4* scp = scale + b * V + lane;
     const uint4* shp = shift + b * V + lane;
 #pragma unroll
@@ -511,8 +586,8 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
   auto step = [&](uint4 (&cur)[VPT], uint4 (&nxt)[VPT], int64_t r) {
     if (r >= cur_hi || r < cur_lo) {
       const int64_t b = sample_of_row(rm, r);
-      cur_lo = rm.offsets ? rm.offsets[b] : b * rm.N;
-      cur_hi = rm.offsets ? rm.offsets[b + 1] : cur_lo + rm.N;
+      cur_lo = rm.offsets ? clamp_row(rm.offsets[b], rm.R) : b * rm.N;
+      cur_hi = rm.offsets ? clamp_row(rm.offsets[b + 1], rm.R) : cur_lo + rm.N;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         sc[j] = scale[b * V + lane + j * 64];
@@ -542,7 +617,7 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
     __builtin_amdgcn_sched_barrier(0);
     load_row(nxt, r + active);
     __builtin_amdgcn_sched_barrier(0);
-    chan_reduce_unit(m, s, n_lane, 64);
+    chan_reduce_wave(m, s, n_lane);
     const float rs = 1.0f / sqrtf(s * inv_d + eps);
     if (lane == 0) { mean[r] = m; rstd[r] = rs; }
     uint4* yr = y + r * V + lane;
@@ -615,7 +690,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < VPT; ++j) sc_raw[j] = scp[j * lpr];
   }
-  float sc1[VPT][EPV];
+  float scl[VPT][EPV];
   float acc_h[VPT][EPV], acc_s[VPT][EPV];   // column partials of dy and dy*xhat
 #pragma unroll
   for (int j = 0; j < VPT; ++j)
@@ -658,9 +733,9 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           const float xh = (fx[k] - mu[i]) * rs[i];
-          const float g = mul_rounded(fg[k], sc1[j][k]);   // same rounding in both passes
+          const float g = grad_g(fg[k], scl[j][k]);
           a += g;
-          c += g * xh;
+          c = __builtin_fmaf(g, xh, c);
         }
       }
       sg[i] = sum_unit(a, unit);
@@ -688,7 +763,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
       const int64_t m = base + static_cast<int64_t>(slot) * RIF + i;
       if (m >= count) continue;
       const int64_t row = first + m * step;
-      const float a = sg[i] * inv_d, c = sgx[i] * inv_d;
+      const RowGrad rg(sg[i], sgx[i], rs[i], inv_d);
       uint4* dxr = dx + row * V + lane;
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
@@ -698,11 +773,10 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
           const float xh = (fx[k] - mu[i]) * rs[i];
-          const float g = mul_rounded(fg[k], sc1[j][k]);   // same rounding in both passes
-          out[k] = rs[i] * ((g - a) - xh * c);
+          out[k] = rg.dx(grad_g(fg[k], scl[j][k]), xh);
           if (COLS) {
             acc_h[j][k] += fg[k];
-            acc_s[j][k] += fg[k] * xh;
+            acc_s[j][k] = __builtin_fmaf(fg[k], xh, acc_s[j][k]);
           }
         }
         store_stream(dxr + j * lpr, E::pack(out));
@@ -715,11 +789,7 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   load_rows(0, xv, gv, mu, rs);
   __builtin_amdgcn_sched_barrier(0);   // every first-row load ahead of the wait below
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    E::unpack(sc_raw[j], sc1[j]);
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) sc1[j][k] += 1.0f;
-  }
+  for (int j = 0; j < VPT; ++j) E::unpack(sc_raw[j], scl[j]);
   process(0, 0);
   int it = 1;
   for (int64_t base = rows_per_iter; base < count; base += rows_per_iter, ++it) {
@@ -774,6 +844,160 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
         const int col = (i - h * V) * EPV + h * 4;
         *reinterpret_cast<float4*>(partial + pidx(TA, t, q, col)) = v;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward row pass for rows of whole waves
+// ---------------------------------------------------------------------------
+// Rows of W whole waves (LPR = 64*W lanes = the workgroup, VPT vectors per
+// lane), one row at a time per workgroup, one workgroup per tile.  Per
+// element: d = x - mean, xhat = d*rstd, g = dy*(1+scale) with one rounding
+// (fma(dy, scale, dy)), the row sums of g and g*xhat, the column partials of
+// dy and dy*xhat; after the row sums, dx = rstd*((g - a) - xhat*c) from the
+// xhat and g kept in registers.  The row sums reach the wave's last lane
+// through DPP (row broadcasts), the waves' sums meet in LDS and every lane
+// adds them in wave order: one barrier per row, fixed order, bitwise
+// repeatable.  The wave sums equal the slot kernel's butterfly sums bit for
+// bit (the same pairs are added, only the operand order of commutative adds
+// differs), so both kernels give the same dx for the same row.
+//
+// Against the slot kernel (which recomputes xhat and g from the stored row in
+// its output pass) this takes about 290 instead of 350 instructions per row
+// and lane at D = 5120 bf16, and it keeps its speed when the engine clock
+// drops: on MI355X the clock falls to 1.6-1.8 GHz for ~2-20 ms after a
+// sustained load starts (deeper the more ALU work per byte the kernels do),
+// and there the video backward call takes ~106-108 us against ~114-118 us for
+// the slot kernel (104-105 against 102 us at the settled 2.4 GHz).
+// COLS = false leaves out the column partials (dx only: the first pass of the
+// two-pass backward).
+
+// Sum over a wave into its last lane (other lanes hold partial sums).
+__device__ __forceinline__ float sum_to_last_lane(float v) {
+  v = v + partner16<0>(v);
+  v = v + partner16<1>(v);
+  v = v + partner16<2>(v);
+  v = v + partner16<3>(v);                  // every lane: its 16-lane row's sum
+  // rows 1 and 3 add rows 0 and 2 (lane 15 of the row below), then rows 2 and
+  // 3 add lane 31: lane 63 = (row3 + row2) + (row1 + row0)
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
+constexpr int ROW_MAX_WAVES = VEC_MAX_NT / 64;
+
+template <int DT, int VPT, bool COLS = true>
+__global__ void __launch_bounds__(VEC_MAX_NT)
+bwd_row_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
+               const uint4* __restrict__ scale, const float* __restrict__ mean,
+               const float* __restrict__ rstd, RowMap rm, Tiling tl, int D,
+               float* __restrict__ partial, uint4* __restrict__ dx) {
+  using E = Elem<DT>;
+  constexpr int EPV = E::EPV;
+  const int LPR = blockDim.x;               // the row's lanes: W whole waves
+  const int W = LPR >> 6;
+  const int V = LPR * VPT;
+  __shared__ float2 red[2][ROW_MAX_WAVES];
+
+  const int64_t t = blockIdx.x;
+  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
+  int64_t b, first, step, count;
+  tile_rows_of(rm, tl, t, b, first, step, count);
+  const int lane = threadIdx.x;
+  const int wave = lane >> 6;
+  const float inv_d = 1.0f / static_cast<float>(D);
+
+  // the sample's scale, unpacked once (g = fma(dy, scale, dy))
+  const uint4* mod = scale + b * V + lane;
+  float scl[VPT][EPV];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) E::unpack(mod[j * LPR], scl[j]);
+  float acc_h[VPT][EPV], acc_s[VPT][EPV];   // column partials of dy and dy*xhat
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) { acc_h[j][k] = 0.f; acc_s[j][k] = 0.f; }
+
+  const int64_t adv = step * V;             // vectors from one of the tile's rows to the next
+  const uint4* xp = x + first * V + lane;
+  const uint4* gp = dy + first * V + lane;
+  uint4* dp = dx + first * V + lane;
+
+  uint4 xv[VPT], gv[VPT];
+  for (int64_t m = 0; m < count; ++m) {
+    float mu, rs;
+    {
+      // The statistics go through vector loads (the offset is made opaque
+      // in a vector register), issued with the row's own loads; as scalar
+      // loads they would be waited for by the barrier's LDS wait.
+      int64_t o = m * step;
+      asm volatile("" : "+v"(o));
+      mu = mean[first + o];
+      rs = rstd[first + o];
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        xv[j] = load_stream(xp + m * adv + j * LPR);
+        gv[j] = load_stream(gp + m * adv + j * LPR);
+      }
+    }
+    float xh[VPT][EPV], g[VPT][EPV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      float d[EPV], fg[EPV];
+      Center<DT>::apply(xv[j], -mu, d);
+      E::unpack(gv[j], fg);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        xh[j][k] = d[k] * rs;
+        g[j][k] = grad_g(fg[k], scl[j][k]);
+        s1 += g[j][k];
+        s2 = __builtin_fmaf(g[j][k], xh[j][k], s2);
+        if (COLS) {
+          acc_h[j][k] += fg[k];
+          acc_s[j][k] = __builtin_fmaf(fg[k], xh[j][k], acc_s[j][k]);
+        }
+      }
+    }
+    float a, c;
+    if (W == 1) {
+      a = sum_wave(s1);
+      c = sum_wave(s2);
+    } else {
+      const int par = static_cast<int>(m & 1);
+      s1 = sum_to_last_lane(s1);
+      s2 = sum_to_last_lane(s2);
+      if ((lane & 63) == 63) red[par][wave] = make_float2(s1, s2);
+      __syncthreads();
+      float2 v = red[par][0];
+      a = v.x; c = v.y;
+      for (int w = 1; w < W; ++w) { v = red[par][w]; a += v.x; c += v.y; }
+    }
+    const RowGrad rg(a, c, rs, inv_d);
+    uint4* dr = dp + m * adv;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      float o[EPV];
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) o[k] = rg.dx(g[j][k], xh[j][k]);
+      store_stream(dr + j * LPR, E::pack(o));
+    }
+  }
+  if constexpr (!COLS) return;
+
+  // tile partials, chunk-major (see pidx)
+  const int64_t TA = tl.tiles_alloc;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int col = (j * LPR + lane) * EPV;
+#pragma unroll
+    for (int k = 0; k < EPV; k += 4) {
+      *reinterpret_cast<float4*>(partial + pidx(TA, t, 0, col + k)) =
+          make_float4(acc_h[j][k], acc_h[j][k + 1], acc_h[j][k + 2], acc_h[j][k + 3]);
+      *reinterpret_cast<float4*>(partial + pidx(TA, t, 1, col + k)) =
+          make_float4(acc_s[j][k], acc_s[j][k + 1], acc_s[j][k + 2], acc_s[j][k + 3]);
     }
   }
 }
@@ -944,18 +1168,18 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
     float a = 0.f, c = 0.f;
     for (int d = threadIdx.x; d < D; d += GEN_NT) {
       const float xh = (E::load1(x, base + d) - mu) * rs;
-      const float g = mul_rounded(E::load1(dy, base + d), 1.0f + E::load1(scale, b * D + d));
-      a += g; c += g * xh;
+      const float g = grad_g(E::load1(dy, base + d), E::load1(scale, b * D + d));
+      a += g; c = __builtin_fmaf(g, xh, c);
     }
-    a = block_sum(a, red[(k++) & 3]) * inv_d;
-    c = block_sum(c, red[(k++) & 3]) * inv_d;
+    a = block_sum(a, red[(k++) & 3]);
+    c = block_sum(c, red[(k++) & 3]);
+    const RowGrad rg(a, c, rs, inv_d);
     for (int d = threadIdx.x; d < D; d += GEN_NT) {
       const float xh = (E::load1(x, base + d) - mu) * rs;
       const float gy = E::load1(dy, base + d);
-      const float g = mul_rounded(gy, 1.0f + E::load1(scale, b * D + d));
-      E::store1(dx, base + d, rs * ((g - a) - xh * c));
+      E::store1(dx, base + d, rg.dx(grad_g(gy, E::load1(scale, b * D + d)), xh));
       partial[pidx(TA, t, 0, d)] += gy;
-      partial[pidx(TA, t, 1, d)] += gy * xh;
+      partial[pidx(TA, t, 1, d)] = __builtin_fmaf(gy, xh, partial[pidx(TA, t, 1, d)]);
     }
   }
 }
@@ -964,9 +1188,7 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // finish: dshift[b,d] / dscale[b,d] = sum of sample b's tile partials
 // ---------------------------------------------------------------------------
 // Both variants add the tiles in an order fixed by the shape and the CU count
-// alone, in fp64 (the narrow one rounds its per-slice sums of at most 8 tiles
-// to fp32 on the way through LDS), and round the result once to the output
-// type, which is the template's DT: the I/O type, or F32 for callers that
+// alone, entirely in fp64, and round the result once to the output type, which is the template's DT: the I/O type, or F32 for callers that
 // want fp32 column sums whatever the I/O type.  Bitwise repeatable, no
 // atomics.  Measured alternatives on MI355X (video shape) and why they lost:
 // one thread walking all tiles of its column (49 us, latency-bound); a
@@ -987,12 +1209,13 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
 
 // Few samples, at most NARROW_MAX_TILES tiles each: one 256-thread workgroup
 // per (sample, 16-column chunk).  Thread (slice, lane) adds tiles slice,
-// slice + 64, ... (ascending, at most 8) for 4 adjacent columns; the 64 slice
-// sums are then added in a fixed two-level order (run r adds slices r, r+8,
-// ..., r+56, then the 8 run sums are added in run order).  320 workgroups on
-// the video shape, every load issued up front over one contiguous run of
-// partials: about one memory round trip.  The LDS layouts keep every access
-// of a wave on distinct banks (rocprofv3 SQ_LDS_BANK_CONFLICT = 0).
+// slice + 64, ... (ascending, at most 8) for 4 adjacent columns in fp64; the
+// 64 slice sums are then added in a fixed two-level order (run r adds slices
+// r, r+8, ..., r+56, then the 8 run sums are added in run order), still in
+// fp64, so the only rounding of a column sum is the final one.  320
+// workgroups on the video shape, every load issued up front over one
+// contiguous run of partials: about one memory round trip.  The LDS arrays
+// are component-major with consecutive lanes on consecutive doubles.
 constexpr int NARROW_LANES = PCOLS / 4;                  // float4 lanes per chunk
 constexpr int NARROW_SLICES = 256 / NARROW_LANES;        // 64
 constexpr int NARROW_PER = 8;                            // tiles per slice
@@ -1006,11 +1229,12 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   using E = Elem<DT>;
   constexpr int LANES = NARROW_LANES, NSLICE = NARROW_SLICES, PER = NARROW_PER;
   constexpr int RUNS = NSLICE / 8;
-  __shared__ float4 sl_h[NSLICE][LANES];    // per-slice sums (fp32: at most PER tiles each)
-  __shared__ float4 sl_s[NSLICE][LANES];
-  // component-major, so a wave's stores are contiguous; each component's
-  // plane is padded by 4 doubles so that the 32 threads of the last step,
-  // one per (component, quantity, lane), read distinct banks
+  constexpr int SPLANE = NSLICE * LANES;    // doubles per component plane of the slice sums
+  __shared__ double sl_h[4][SPLANE];        // per-slice sums, component-major
+  __shared__ double sl_s[4][SPLANE];
+  // each component's plane of run sums is padded by 4 doubles so that the 32
+  // threads of the last step, one per (component, quantity, lane), read
+  // distinct banks
   constexpr int RUN_PLANE = RUNS * LANES + 4;
   __shared__ double run_h[4][RUN_PLANE];
   __shared__ double run_s[4][RUN_PLANE];
@@ -1042,18 +1266,19 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
     h[0] += vh[u].x; h[1] += vh[u].y; h[2] += vh[u].z; h[3] += vh[u].w;
     sc[0] += vs[u].x; sc[1] += vs[u].y; sc[2] += vs[u].z; sc[3] += vs[u].w;
   }
-  sl_h[slice][lane] = make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]),
-                                  static_cast<float>(h[2]), static_cast<float>(h[3]));
-  sl_s[slice][lane] = make_float4(static_cast<float>(sc[0]), static_cast<float>(sc[1]),
-                                  static_cast<float>(sc[2]), static_cast<float>(sc[3]));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    sl_h[w][slice * LANES + lane] = h[w];
+    sl_s[w][slice * LANES + lane] = sc[w];
+  }
   __syncthreads();
   if (slice < RUNS) {
     double a[4] = {0.0, 0.0, 0.0, 0.0}, c[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int q = 0; q < NSLICE / RUNS; ++q) {
-      const float4 x = sl_h[slice + q * RUNS][lane], y = sl_s[slice + q * RUNS][lane];
-      a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
-      c[0] += y.x; c[1] += y.y; c[2] += y.z; c[3] += y.w;
+      const int i = (slice + q * RUNS) * LANES + lane;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) { a[w] += sl_h[w][i]; c[w] += sl_s[w][i]; }
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -1134,8 +1359,8 @@ finish_tiles_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, int
 constexpr int PRO_NT = 1024;
 
 __global__ void __launch_bounds__(PRO_NT)
-varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile_rows,
-                    int64_t* __restrict__ tile_start) {
+varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t R, int64_t tile_rows,
+                    int64_t tiles_alloc, int64_t* __restrict__ tile_start) {
   __shared__ int64_t scan[PRO_NT];
   __shared__ int64_t carry;
   if (threadIdx.x == 0) carry = 0;
@@ -1144,7 +1369,7 @@ varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile
     const int64_t b = base + threadIdx.x;
     int64_t cnt = 0;
     if (b < B) {
-      const int64_t n = offsets[b + 1] - offsets[b];
+      const int64_t n = clamped_span(offsets[b], offsets[b + 1], R).n;
       cnt = n > 0 ? (n + tile_rows - 1) / tile_rows : 0;
     }
     scan[threadIdx.x] = cnt;
@@ -1156,13 +1381,16 @@ varlen_tiles_kernel(const int64_t* __restrict__ offsets, int64_t B, int64_t tile
       scan[threadIdx.x] += v;
       __syncthreads();
     }
-    if (b < B) tile_start[b] = carry + scan[threadIdx.x] - cnt;   // exclusive
+    // exclusive, capped at the partials' tile capacity (reached only by a
+    // malformed table whose samples overlap)
+    if (b < B) tile_start[b] = min(carry + scan[threadIdx.x] - cnt, tiles_alloc);
     __syncthreads();
     if (threadIdx.x == PRO_NT - 1) carry += scan[PRO_NT - 1];
     __syncthreads();
   }
-  if (threadIdx.x == 0) tile_start[B] = carry;
+  if (threadIdx.x == 0) tile_start[B] = min(carry, tiles_alloc);
 }
+
 
 // ---------------------------------------------------------------------------
 // plans and launchers
@@ -1195,6 +1423,20 @@ static hipError_t fwd_vec_launch(const void* x, const void* shift, const void* s
                      dim3(vp.nt), lds, stream, static_cast<const uint4*>(x),
                      static_cast<const uint4*>(shift), static_cast<const uint4*>(scale), eps, rm, V,
                      static_cast<int>(D), vp.lpr, rows_per_wg, static_cast<uint4*>(y), mean, rstd);
+  return hipGetLastError();
+}
+
+// Backward row kernel launch: rows of vp.lpr lanes (whole waves, one row slot
+// per workgroup), one workgroup per tile.
+template <int DT, int VPT, bool COLS>
+static hipError_t bwd_row_launch(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd, const RowMap& rm,
+                                 int64_t D, const VecPlan& vp, const Tiling& tl, float* partial,
+                                 hipStream_t stream, void* dx) {
+  hipLaunchKernelGGL((bwd_row_kernel<DT, VPT, COLS>), dim3(static_cast<unsigned>(tl.tiles_max)),
+                     dim3(vp.lpr), 0, stream, static_cast<const uint4*>(dy),
+                     static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
+                     tl, static_cast<int>(D), partial, static_cast<uint4*>(dx));
   return hipGetLastError();
 }
 
@@ -1292,6 +1534,37 @@ static hipError_t fwd_dispatch(const void* x, const void* shift, const void* sca
   return hipGetLastError();
 }
 
+// The vectorised backward row pass (dx, and the tile partials when COLS):
+// the row kernel for rows of whole waves, else the slot kernel.  The fused
+// and the two-pass backward both come through here, so their dx is the same.
+template <int DT, bool COLS>
+static hipError_t bwd_rows(const void* dy, const void* x, const void* scale, const float* mean,
+                           const float* rstd, const RowMap& rm, int64_t D, const VecPlan& vp,
+                           const Tiling& tl, float* partial, hipStream_t stream, void* dx) {
+  const bool row = vp.nt == vp.lpr && vp.lpr % 64 == 0;
+#define ADALN_ROWS_CASE(N)                                                                         \
+  case N:                                                                                          \
+    return row ? bwd_row_launch<DT, N, COLS>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial,    \
+                                             stream, dx)                                           \
+               : bwd_vec_launch<DT, N, COLS>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial,    \
+                                             stream, dx);
+  switch (vp.vpt) {
+    ADALN_ROWS_CASE(1) ADALN_ROWS_CASE(2) ADALN_ROWS_CASE(3) ADALN_ROWS_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef ADALN_ROWS_CASE
+}
+
+template <int DT>
+static hipError_t bwd_gen_launch(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd, const RowMap& rm,
+                                 int64_t D, const Tiling& tl, float* partial, hipStream_t stream,
+                                 void* dx) {
+  hipLaunchKernelGGL((bwd_gen_kernel<DT>), dim3(static_cast<unsigned>(tl.tiles_max)), dim3(GEN_NT),
+                     0, stream, dy, x, scale, mean, rstd, rm, tl, static_cast<int>(D), partial, dx);
+  return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
                                 const float* partial, hipStream_t stream, void* dscale,
@@ -1306,24 +1579,12 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
   hipError_t e = hipSuccess;
   if (rm.offsets != nullptr) {
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       tl.tile_rows, tl.tile_start);
+                       rm.R, tl.tile_rows, tl.tiles_alloc, tl.tile_start);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rm.R > 0 && tl.tiles_max > 0) {
-    if (vec) {
-      switch (vp.vpt) {
-        case 1: e = bwd_vec_launch<DT, 1>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-        case 2: e = bwd_vec_launch<DT, 2>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-        case 3: e = bwd_vec_launch<DT, 3>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-        case 4: e = bwd_vec_launch<DT, 4>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-        default: return hipErrorInvalidValue;
-      }
-    } else {
-      hipLaunchKernelGGL((bwd_gen_kernel<DT>), dim3(static_cast<unsigned>(tl.tiles_max)),
-                         dim3(GEN_NT), 0, stream, dy, x, scale, mean, rstd, rm, tl,
-                         static_cast<int>(D), partial, dx);
-      e = hipGetLastError();
-    }
+    e = vec ? bwd_rows<DT, true>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx)
+            : bwd_gen_launch<DT>(dy, x, scale, mean, rstd, rm, D, tl, partial, stream, dx);
     if (e != hipSuccess) return e;
   }
   return sums_f32 ? finish_launch<F32>(rm, D, tl, partial, stream, dscale, dshift)
@@ -1362,17 +1623,11 @@ static hipError_t bwd_twopass_dispatch(const void* dy, const void* x, const void
   hipError_t e = hipSuccess;
   if (rm.offsets != nullptr) {
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       tl.tile_rows, tl.tile_start);
+                       rm.R, tl.tile_rows, tl.tiles_alloc, tl.tile_start);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rm.R > 0 && tl.tiles_max > 0) {
-    switch (vp.vpt) {
-      case 1: e = bwd_vec_launch<DT, 1, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-      case 2: e = bwd_vec_launch<DT, 2, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-      case 3: e = bwd_vec_launch<DT, 3, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-      case 4: e = bwd_vec_launch<DT, 4, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx); break;
-      default: return hipErrorInvalidValue;
-    }
+    e = bwd_rows<DT, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx);
     if (e != hipSuccess) return e;
     const int V = static_cast<int>(D / Elem<DT>::EPV);
     Tiling chunks = tl;

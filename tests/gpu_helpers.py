@@ -185,6 +185,41 @@ def check_rows(pd, out, rows, eps=None, strict=True):
     return res
 
 
+def check_every_row(pd, out, eps=None, strict=True, chunk=2048):
+    """check_rows over every row of the problem, in chunks of `chunk` rows so
+    that the oracle's fp64 arrays stay small; the normwise errors are taken
+    over the whole tensor (max |got - ref| over max |ref| of all rows)."""
+    p = pd.problem
+    eps = p.eps if eps is None else eps
+    t = TOL[p.dtype]
+    err = {"y": 0.0, "dx": 0.0}
+    ref_max = {"y": 0.0, "dx": 0.0}
+    res = {"y_abs": 0.0, "dx_abs": 0.0, "mean": 0.0, "rstd": 0.0, "rows": p.R}
+    for lo in range(0, p.R, chunk):
+        rows = np.arange(lo, min(p.R, lo + chunk), dtype=np.int64)
+        x, dy, shift, scale, off = _rows_problem(pd, rows)
+        y_ref, mean_ref, rstd_ref = oracle.adaln_fwd(x, shift, scale, eps, off)
+        dx_ref, _, _ = oracle.adaln_bwd(dy, x, scale, eps, off)
+        sl = slice(int(rows[0]), int(rows[-1]) + 1)
+        y = to_host64(out["y"][sl])
+        dx = to_host64(out["dx"][sl])
+        mean = to_host64(out["mean"][sl])
+        rstd = to_host64(out["rstd"][sl])
+        res["y_abs"] = max(res["y_abs"], assert_abs(y, y_ref, t["abs"], "y", p.dtype == "bf16", strict))
+        res["dx_abs"] = max(res["dx_abs"], assert_abs(dx, dx_ref, t["abs"], "dx", p.dtype == "bf16", strict))
+        for k, g, r in (("y", y, y_ref), ("dx", dx, dx_ref)):
+            err[k] = max(err[k], float(np.abs(g - r).max()))
+            ref_max[k] = max(ref_max[k], float(np.abs(r).max()))
+        row_scale = np.abs(mean_ref) + 1.0 / rstd_ref
+        res["mean"] = max(res["mean"], assert_abs(np.abs(mean - mean_ref) / row_scale, 0.0, STAT_TOL, "mean"))
+        res["rstd"] = max(res["rstd"], assert_abs(np.abs(rstd - rstd_ref) / rstd_ref, 0.0, STAT_TOL, "rstd"))
+    for k in ("y", "dx"):
+        e = err[k] / ref_max[k] if ref_max[k] > 0 else err[k]
+        assert e <= t["norm"], f"{k}: normwise error {e:.3e} > {t['norm']:.1e}"
+        res[k + "_norm"] = e
+    return res
+
+
 def check_samples(pd, out, samples, eps=None, mean_rounding=False):
     """dscale and dshift of the given samples (full column sums) against the oracle.
 

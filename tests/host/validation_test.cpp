@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <limits>
+#include <vector>
 
 #include "adaln.h"
 #include "../../diffusion_transformer_adaln_amd/csrc/adaln_internal.hpp"
@@ -344,7 +345,49 @@ static void test_plans() {
         }
 }
 
+// Device offsets are trusted but clamped where the kernels read them: every
+// sample's clamped span lies inside [0, R], and the packed backward's tile
+// table (per-sample tile counts from the clamped spans, prefix sums capped at
+// the partials' capacity, as the prologue computes it), mapped to rows the
+// way the row pass maps them (tile k of a sample takes rows k, k + tiles, ...),
+// never reaches a row outside [0, R) or a tile at or past tiles_alloc, for
+// malformed tables too (negative, past R, decreasing, overlapping).
+static void test_offset_clamp() {
+  EXPECT(adaln::clamp_row(-5, 10) == 0 && adaln::clamp_row(11, 10) == 10 && adaln::clamp_row(7, 10) == 7,
+         "clamp_row");
+  const int64_t R = 1000, D = 64;
+  const int cus = 256;
+  const std::vector<std::vector<int64_t>> tables = {
+      {0, 100, 1000},                      // well formed
+      {-50, 400, 2000},                    // ends outside [0, R]
+      {0, 900, 100, 1000},                 // decreasing
+      {0, 1000, 0, 1000, 0, 1000},         // overlapping samples
+      {5000, -7, 3000, 1000},              // nothing sensible
+      {INT64_MIN, INT64_MAX},
+  };
+  for (const auto& o : tables) {
+    const int64_t B = static_cast<int64_t>(o.size()) - 1;
+    const adaln::WorkspaceLayout w = adaln::bwd_workspace_layout(B, R, D, cus, true, 0);
+    int64_t start = 0;
+    bool ok = true;
+    for (int64_t b = 0; b < B; ++b) {
+      const adaln::RowSpan sp = adaln::clamped_span(o[b], o[b + 1], R);
+      ok = ok && sp.lo >= 0 && sp.n >= 0 && sp.lo + sp.n <= R;
+      const int64_t cnt = sp.n > 0 ? (sp.n + w.tile_rows - 1) / w.tile_rows : 0;
+      const int64_t t0 = start < w.tiles_alloc ? start : w.tiles_alloc;
+      const int64_t t1 = start + cnt < w.tiles_alloc ? start + cnt : w.tiles_alloc;
+      start += cnt;
+      const int64_t tiles = t1 - t0;
+      for (int64_t k = 0; k < tiles; ++k)
+        for (int64_t r = sp.lo + k; r < sp.lo + sp.n; r += tiles) ok = ok && r >= 0 && r < R;
+      ok = ok && t1 <= w.tiles_alloc && t0 <= t1;
+    }
+    EXPECT(ok, "offset table of %lld samples leaves [0, R) or the tile capacity", (long long)B);
+  }
+}
+
 int main() {
+  test_offset_clamp();
   test_plans();
   test_forward();
   test_forward_varlen();

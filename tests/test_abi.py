@@ -1,5 +1,5 @@
-"""The C-ABI library loads, exports every entry point include/adaln.h and
-include/adaln_sched.h declare, and rejects bad arguments before touching a device (no kernels
+"""The C-ABI library loads, exports every entry point include/adaln.h,
+include/adaln_sched.h and include/adaln_probe.h declare, and rejects bad arguments before touching a device (no kernels
 are launched here, and no HIP call is reached on these paths)."""
 
 import ctypes
@@ -13,7 +13,7 @@ import diffusion_transformer_adaln_amd as adaln
 from diffusion_transformer_adaln_amd.build import LIB_PATH
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("adaln.h", "adaln_sched.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("adaln.h", "adaln_sched.h", "adaln_probe.h")]
 
 
 def declared_functions():
@@ -125,7 +125,7 @@ def test_workspace_query_rejects_bad_sizes(lib):
 
 
 def test_headers_compile_as_c_and_link(tmp_path, lib):
-    """A plain C11 program includes both headers, links libadaln.so and calls
+    """A plain C11 program includes the headers, links libadaln.so and calls
     the host-only entry points: the ABI is usable from C without torch."""
     import shutil
 
@@ -137,6 +137,7 @@ def test_headers_compile_as_c_and_link(tmp_path, lib):
 #include <stdio.h>
 #include "adaln.h"
 #include "adaln_sched.h"
+#include "adaln_probe.h"
 int main(void) {
   if (adaln_abi_version() != ADALN_ABI_VERSION) return 1;
   if (adaln_status_str(ADALN_ERR_ALIASING) == NULL) return 2;
@@ -151,8 +152,8 @@ int main(void) {
     typedef void (*fn_t)(void);
     fn_t fns[] = {(fn_t)adaln_fwd, (fn_t)adaln_bwd, (fn_t)adaln_fwd_varlen, (fn_t)adaln_bwd_varlen,
                   (fn_t)adaln_bwd_twopass, (fn_t)adaln_bwd_workspace_size, (fn_t)adaln_sched_plan,
-                  (fn_t)adaln_cost_fit};
-    for (int i = 0; i < 8; ++i) if (fns[i] == NULL) return 5;
+                  (fn_t)adaln_cost_fit, (fn_t)adaln_probe_stream};
+    for (int i = 0; i < 9; ++i) if (fns[i] == NULL) return 5;
   }
   puts("ok");
   return 0;
@@ -169,3 +170,18 @@ int main(void) {
     assert build.returncode == 0, build.stderr[-3000:]
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0 and run.stdout.strip() == "ok", (run.returncode, run.stdout, run.stderr[-2000:])
+
+
+def test_probe_rejects_bad_arguments(lib):
+    """The ceiling probe validates before any device call: sizes not a multiple
+    of 16, bad grid shapes, missing or misaligned buffers, unknown modes."""
+    st = lambda mode=0, a=FAKE, b=FAKE * 2, out=FAKE * 3, n=4096, wg=1, u=4: lib.adaln_probe_stream(
+        mode, P(a), P(b), P(out), n, wg, u, None)
+    bad = 1                      # ADALN_ERR_INVALID_ARG
+    assert st(n=100) == bad and st(n=-16) == bad
+    assert st(wg=0) == bad and st(wg=17) == bad
+    assert st(u=3) == bad and st(u=16) == bad
+    assert st(mode=7) == bad and st(mode=-1) == bad
+    assert st(a=0) == bad and st(out=0) == bad
+    assert st(mode=1, b=0) == bad
+    assert st(a=FAKE + 8) == bad

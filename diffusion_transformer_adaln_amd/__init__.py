@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     adaln_abi_version,
     adaln_bwd,
     adaln_bwd_f32sums,
+    adaln_bwd_noalloc,
     adaln_bwd_twopass,
     adaln_bwd_varlen,
     adaln_bwd_varlen_f32sums,

@@ -37,6 +37,7 @@ EXPORTED = (
     "adaln_bwd_f32sums",
     "adaln_bwd_varlen_f32sums",
     "adaln_bwd_workspace_size",
+    "adaln_bwd_noalloc",
     "adaln_status_str",
     "adaln_abi_version",
     "adaln_sched_batch_size",
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_bwd_twopass.restype = ctypes.c_int
     lib.adaln_bwd_f32sums.argtypes = lib.adaln_bwd.argtypes
     lib.adaln_bwd_f32sums.restype = ctypes.c_int
+    lib.adaln_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P]
+    lib.adaln_bwd_noalloc.restype = ctypes.c_int
     lib.adaln_sched_batch_size.argtypes = [_I64, _I64, _I64, ctypes.c_double]
     lib.adaln_sched_batch_size.restype = _I64
     lib.adaln_sched_plan.argtypes = [_P, _I64, _I64, _I64, ctypes.c_double, _P, _P]
@@ -367,6 +370,32 @@ def _bwd_dense(fn, dy, x, scale, mean, rstd, workspace, dx, dscale, dshift, stre
              _dtype_code(x.dtype), _ptr(workspace), wbytes, _stream(dev, stream), _ptr(dx),
              _ptr(dscale), _ptr(dshift))
     _raise(fn, st)
+    return dx, dscale, dshift
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def adaln_bwd_noalloc(dy, x, scale, mean, rstd, dx, dscale, dshift, stream=None):
+    """adaln_bwd through the entry point that allocates nothing: the outputs
+    are the caller's (this wrapper allocates nothing either) and the workspace
+    is the library's static device array.  Returns (dx, dscale, dshift)."""
+    if x.dim() != 3 or dy.shape != x.shape:
+        raise ValueError("adaln_bwd_noalloc expects dy and x of shape [B, N, D]")
+    B, N, D = x.shape
+    if dy.dtype is not x.dtype:
+        raise TypeError(f"dy must be {x.dtype}, got {dy.dtype}")
+    _expect(scale, (B, D), x.dtype, "scale")
+    _expect_stats(mean, B * N, "mean")
+    _expect_stats(rstd, B * N, "rstd")
+    _expect(dx, x.shape, x.dtype, "dx")
+    _expect(dscale, (B, D), x.dtype, "dscale")
+    _expect(dshift, (B, D), x.dtype, "dshift")
+    dev = _check_dev(dy, x, scale, mean, rstd, dx, dscale, dshift)
+    lib = load_library()
+    st = _on(dev, lib.adaln_bwd_noalloc, _ptr(dy), _ptr(x), _ptr(scale), _ptr(mean), _ptr(rstd), B, N, D,
+             _dtype_code(x.dtype), _stream(dev, stream), _ptr(dx), _ptr(dscale), _ptr(dshift))
+    _raise("adaln_bwd_noalloc", st)
     return dx, dscale, dshift
 
 

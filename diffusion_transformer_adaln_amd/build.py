@@ -5,8 +5,10 @@
 Compiles csrc/adaln_api.cpp (host: validation and dispatch),
 csrc/adaln_plan.cpp (host: row layouts, backward tiling, workspace layout),
 csrc/adaln_sched.cpp (host: batch scheduling and cost model),
-csrc/adaln_kernels.hip (gfx950 kernels) and csrc/adaln_probe.hip (streaming
-ceiling probes, include/adaln_probe.h) with hipcc into one shared library
+csrc/adaln_kernels.hip (gfx950 kernels), csrc/adaln_noalloc.hip (the
+backward entry point that allocates nothing) and csrc/adaln_probe.hip
+(streaming ceiling probes, include/adaln_probe.h) with hipcc into one shared
+library
 next to this file.  Every call recompiles.
 """
 
@@ -25,7 +27,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = [os.path.join(CSRC, "adaln_api.cpp"), os.path.join(CSRC, "adaln_plan.cpp"),
            os.path.join(CSRC, "adaln_sched.cpp"), os.path.join(CSRC, "adaln_kernels.hip"),
-           os.path.join(CSRC, "adaln_probe.hip")]
+           os.path.join(CSRC, "adaln_probe.hip"), os.path.join(CSRC, "adaln_noalloc.hip")]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 HIPCC_FLAGS = [

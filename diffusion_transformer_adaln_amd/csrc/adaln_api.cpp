@@ -182,6 +182,22 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
 
 }  // namespace
 
+namespace adaln {
+// The dense backward with a workspace the caller (or the no-allocation entry
+// point's static scratch) provides; adaln_bwd's body.
+adaln_status_t bwd_dense_with_workspace(const void* dy, const void* x, const void* scale,
+                                        const float* mean, const float* rstd, int64_t B, int64_t N,
+                                        int64_t D, adaln_dtype_t dtype, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream, void* dx,
+                                        void* dscale, void* dshift) {
+  if (N < 0 || B < 1) return ADALN_ERR_INVALID_ARG;
+  int64_t R;
+  if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
+  return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
+                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFused);
+}
+}  // namespace adaln
+
 ADALN_EXPORT adaln_status_t adaln_fwd(const void* x, const void* shift, const void* scale,
                                       float eps, int64_t B, int64_t N, int64_t D,
                                       adaln_dtype_t dtype, hipStream_t stream, void* y,
@@ -216,11 +232,8 @@ ADALN_EXPORT adaln_status_t adaln_bwd(const void* dy, const void* x, const void*
                                       int64_t D, adaln_dtype_t dtype, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream, void* dx,
                                       void* dscale, void* dshift) {
-  if (N < 0 || B < 1) return ADALN_ERR_INVALID_ARG;
-  int64_t R;
-  if (!mul_ok(B, N, &R)) return ADALN_ERR_UNSUPPORTED_SHAPE;
-  return bwd_common(dy, x, scale, mean, rstd, nullptr, B, N, R, D, dtype, workspace,
-                    workspace_bytes, stream, dx, dscale, dshift, BwdMode::kFused);
+  return adaln::bwd_dense_with_workspace(dy, x, scale, mean, rstd, B, N, D, dtype, workspace,
+                                         workspace_bytes, stream, dx, dscale, dshift);
 }
 
 ADALN_EXPORT adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale,

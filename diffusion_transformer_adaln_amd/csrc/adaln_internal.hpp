@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/adaln.h"
+
 namespace adaln {
 
 enum DType : int { F32 = 0, BF16 = 1 };
@@ -130,5 +132,13 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense);
+
+// adaln_bwd with the workspace given as a pointer and size (shared by adaln_bwd
+// and the no-allocation entry point).
+adaln_status_t bwd_dense_with_workspace(const void* dy, const void* x, const void* scale,
+                                        const float* mean, const float* rstd, int64_t B, int64_t N,
+                                        int64_t D, adaln_dtype_t dtype, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream, void* dx,
+                                        void* dscale, void* dshift);
 
 }  // namespace adaln

@@ -33,7 +33,8 @@
  *
  * Ownership.  Every pointer is a device pointer owned by the caller; the
  * library never allocates, frees or synchronises, and keeps no state except
- * a per-device cache of device properties filled on first use.  Every call
+ * a per-device cache of device properties filled on first use (and, for
+ * adaln_bwd_noalloc, a static device array and its per-device address).  Every call
  * is enqueued asynchronously on `stream` (NULL = the null stream) and returns
  * as soon as its kernels are enqueued.  Calls on different streams may run
  * concurrently as long as their buffers are disjoint.
@@ -67,8 +68,8 @@
 extern "C" {
 #endif
 
-/* 2: adds adaln_bwd_f32sums and adaln_bwd_varlen_f32sums */
-#define ADALN_ABI_VERSION 2
+/* 2: adds adaln_bwd_f32sums and adaln_bwd_varlen_f32sums; 3: adds adaln_bwd_noalloc */
+#define ADALN_ABI_VERSION 3
 
 /* Element type of x, y, dy, dx, shift, scale, dscale, dshift. */
 typedef enum {
@@ -238,6 +239,30 @@ adaln_status_t adaln_bwd_twopass(const void* dy, const void* x, const void* scal
                                  int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream,
                                  void* dx, void* dscale, void* dshift);
+
+/*
+ * adaln_bwd_noalloc -- adaln_bwd without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.
+ *
+ * The workspace comes from a static device array of the library,
+ * ADALN_NOALLOC_SCRATCH_BYTES (32 MiB) on every device the library runs on,
+ * held until the process ends; the call itself allocates nothing.  Problems
+ * whose adaln_bwd_workspace_size() exceeds it return
+ * ADALN_ERR_WORKSPACE_TOO_SMALL before anything is launched (32 MiB holds the
+ * workspace of B = 1, N = 64,000, D = 5120 and of 229,368 rows at D = 3072).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device race and give undefined dscale and dshift.  Arguments,
+ * outputs, launches, results (bit for bit) and the other errors as in
+ * adaln_bwd; ADALN_ERR_HIP also if the array's device address cannot be
+ * looked up on first use on a device.
+ */
+#define ADALN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+adaln_status_t adaln_bwd_noalloc(const void* dy, const void* x, const void* scale,
+                                 const float* mean, const float* rstd,
+                                 int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
+                                 hipStream_t stream, void* dx, void* dscale, void* dshift);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* adaln_status_str(adaln_status_t status);

@@ -42,7 +42,7 @@ def test_header_matches_binding_and_exports(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.adaln_abi_version() == 2
+    assert lib.adaln_abi_version() == 3
     for code, name in adaln._lib.STATUS_NAMES.items():
         assert adaln.adaln_status_str(code) == name
     assert adaln.adaln_status_str(99) == "ADALN_ERR_UNKNOWN"

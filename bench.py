@@ -31,7 +31,18 @@ pair does not bracket a single call); `per_call_us` gives the 10th, 50th and
 `device` records the GPU's name, architecture, CU count and memory (a
 partitioned device shows fewer CUs and a slice of the bandwidth).
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same
-workload's rows on one host core.
+workload's rows on one host core, and reports the GPU path's errors on the
+rows it computed (y, dx, rstd against the oracle: `errors`).
+
+`ceilings` measures what the device delivers for the operator's access
+mixes with the library's streaming probes (include/adaln_probe.h), on
+buffers of the workload's own [R, D] size, after the timed region: a copy
+(one read, one write: the forward's mix) and two reads to one write (the
+backward row pass's), each the best of a small sweep of launch shapes.
+`step_gbs` is the rate a step would reach if its forward bytes moved at the
+copy rate and its backward bytes at the two-to-one rate, and
+`pct_of_copy_ceiling` is `value` against it.  `versions` records ROCm,
+HIP and torch, and `device.compute_partition` the partition mode.
 
 `--bwd twopass` runs the backward through adaln_bwd_twopass instead (dx
 pass, then a separate D-tile column pass that reads dy and x again): the
@@ -139,11 +150,16 @@ def saved_activation_bytes(fn, *args):
     return out, sum(seen.values())
 
 
-def cpu_baseline(pd, seconds):
+def cpu_baseline(pd, seconds, gpu_rows=None):
     """fp64 oracle on successive 128-row blocks of the workload (wrapping
     around to the first row after the last) until about `seconds` of CPU
     time; rows are independent, and each block's column sums are taken over
-    its own rows (the same per-row work as the full sums)."""
+    its own rows (the same per-row work as the full sums).
+
+    gpu_rows(lo, hi) -> (y, dx, rstd) as float64 arrays, when given: the GPU
+    path's outputs of those rows, compared with the oracle's for the blocks of
+    the first pass (errors: max abs error of y and dx, max relative error of
+    rstd)."""
     import numpy as np
 
     import oracle
@@ -152,6 +168,7 @@ def cpu_baseline(pd, seconds):
     rows_done, t_used = 0, 0.0
     block = 128
     start = 0
+    err = {"y_max_abs": 0.0, "dx_max_abs": 0.0, "rstd_max_rel": 0.0, "rows": 0}
     while t_used < seconds:
         if start >= p.R:
             start = 0
@@ -164,9 +181,15 @@ def cpu_baseline(pd, seconds):
         sc = oracle.decode(pd.scale[b:b + 1], p.dtype)
         off = np.array([0, hi - lo], dtype=np.int64)
         t0 = time.process_time()
-        oracle.adaln_fwd(x, sh, sc, p.eps, off)
-        oracle.adaln_bwd(dy, x, sc, p.eps, off)
+        y_ref, _, rstd_ref = oracle.adaln_fwd(x, sh, sc, p.eps, off)
+        dx_ref, _, _ = oracle.adaln_bwd(dy, x, sc, p.eps, off)
         t_used += time.process_time() - t0
+        if gpu_rows is not None and rows_done < p.R:
+            y, dx, rstd = gpu_rows(lo, hi)
+            err["y_max_abs"] = max(err["y_max_abs"], float(np.abs(y - y_ref).max()))
+            err["dx_max_abs"] = max(err["dx_max_abs"], float(np.abs(dx - dx_ref).max()))
+            err["rstd_max_rel"] = max(err["rstd_max_rel"], float((np.abs(rstd - rstd_ref) / rstd_ref).max()))
+            err["rows"] += hi - lo
         rows_done += hi - lo
         start = hi
     import workloads
@@ -178,7 +201,7 @@ def cpu_baseline(pd, seconds):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
     except OSError:
         pass
-    return {
+    out = {
         "value": round(rows_done * per_row / t_used / 1e9, 4),
         "unit": "GB/s",
         "rows_per_s": round(rows_done / t_used, 1),
@@ -190,6 +213,76 @@ def cpu_baseline(pd, seconds):
                   f"{rows_done / p.R:.2f} passes over its {p.R} rows), 128-row blocks, "
                   f"{t_used:.1f} s of CPU time on one core",
     }
+    if gpu_rows is not None:
+        out["errors"] = {k: (v if k == "rows" else float(f"{v:.3e}")) for k, v in err.items()}
+        out["errors"]["what"] = ("GPU path vs fp64 oracle on the rows above (first pass): max |y - ref|, "
+                                 "max |dx - ref|, max |rstd - ref| / ref")
+    return out
+
+
+PROBE_SHAPES = [(wg, u) for wg in (1, 2, 4) for u in (1, 2, 4, 8)]
+
+
+def ceilings(adaln, torch, np, runner, nbytes_fwd, nbytes_bwd):
+    """Streaming ceilings for the workload's [R, D] tensor size: the best
+    copy (1 read : 1 write) and two-to-one (2 reads : 1 write) rates over the
+    launch shapes in PROBE_SHAPES, timed like the operator's calls (blocks of
+    back-to-back passes over rotating resident copies, one event pair per
+    block), on the runner's own buffers (x, dy read; y, dx written)."""
+    sets = runner.sets
+    nb = (runner.p.R * runner.p.D * runner.p.esize) // 16 * 16
+    if nb == 0:
+        return None
+    u8 = lambda t: t.view(torch.uint8).view(-1)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    res = {}
+    for mode, k in (("copy", 2), ("two_to_one", 3)):
+        best = None
+        for wg, un in PROBE_SHAPES:
+            times = []
+            for rep in range(3):
+                e0, e1 = ev(), ev()
+                e0.record()
+                for i in range(6):
+                    s = sets[(rep * 6 + i) % len(sets)]
+                    adaln.adaln_probe_stream(mode, u8(s["x"]), u8(s["dy"]), u8(s["y"] if mode == "copy" else s["dx"]),
+                                             wg, un, nbytes=nb)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / 6)
+            gbs = k * nb / (float(np.median(times)) * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, wg, un)
+        res[mode] = {"gbs": round(best[0], 1), "wg_per_cu": best[1], "unroll": best[2]}
+    step = (nbytes_fwd + nbytes_bwd) / (nbytes_fwd / res["copy"]["gbs"] + nbytes_bwd / res["two_to_one"]["gbs"])
+    res["step_gbs"] = round(step, 1)
+    return res
+
+
+def versions(torch):
+    rocm = "unknown"
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"rocm": rocm, "hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
+
+
+def compute_partition(cus):
+    """The device's compute partition mode from sysfs when it is readable, else
+    what the visible CU count implies (256 CUs: the whole chip, SPX)."""
+    import glob
+
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/current_compute_partition")):
+        try:
+            with open(path) as f:
+                mode = f.read().strip()
+            if mode:
+                return mode
+        except OSError:
+            continue
+    return "SPX (inferred: 256 CUs visible)" if cus == 256 else f"unknown ({cus} CUs visible)"
 
 
 class Runner:
@@ -509,6 +602,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    ceil = None
+    if args.impl == "hip":
+        ceil = ceilings(adaln, torch, np, main_r, nbytes["fwd"], nbytes["bwd"])
+
     traffic = read_traffic(args.traffic_file, args.config) if (args.bwd, args.impl) == ("fused", "hip") else None
     bwd_name = {"fused": "adaln_bwd", "twopass": "adaln_bwd_twopass", "f32sums": "adaln_bwd_f32sums"}[args.bwd]
     if not all(pd.problem.dense for pd in pds):      # packed samples go through the varlen entry points
@@ -538,7 +635,9 @@ def main():
                    "D": p.D, "impl": args.impl, "bwd": bwd_name, "parallelism": "single GPU"},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count,
-                   "hbm_gib": round(props.total_memory / 2 ** 30, 1)},
+                   "hbm_gib": round(props.total_memory / 2 ** 30, 1),
+                   "compute_partition": compute_partition(props.multi_processor_count)},
+        "versions": versions(torch),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "rows_per_s": round(rows_per_s, 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 2),
@@ -553,8 +652,26 @@ def main():
                      "achieved": round(bwd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(bwd_gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
     }
+    if ceil is not None:
+        ceil["pct_of_copy_ceiling"] = round(100 * gbs / ceil["step_gbs"], 2)
+        out["ceilings"] = ceil
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pd, args.cpu_seconds)
+        gpu_rows = None
+        if args.impl == "hip":
+            s0 = main_r.sets[0]
+            main_r.fwd(s0)
+            main_r.bwd(s0)
+            torch.cuda.synchronize()
+
+            def host64(t):
+                if t.dtype == torch.bfloat16:
+                    u = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16
+                    return u.view(np.float32).astype(np.float64)
+                return t.cpu().numpy().astype(np.float64)
+
+            def gpu_rows(lo, hi):
+                return host64(s0["y"][lo:hi]), host64(s0["dx"][lo:hi]), host64(s0["rstd"][lo:hi])
+        out["cpu_baseline"] = cpu_baseline(pd, args.cpu_seconds, gpu_rows)
     print(json.dumps(out), flush=True)
 
 

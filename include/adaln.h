@@ -113,7 +113,9 @@ adaln_status_t adaln_fwd(const void* x, const void* shift, const void* scale, fl
                          hipStream_t stream, void* y, float* mean, float* rstd);
 
 /*
- * adaln_bwd_workspace_size -- bytes of device workspace every backward entry
+ * adaln_bwd_workspace_size -- infrastructure (no passage of the summary
+ * defines it): the storage of section 2.B's two-stage column reduction.
+ * Bytes of device workspace every backward entry
  * point (adaln_bwd, adaln_bwd_varlen, their *_f32sums variants and
  * adaln_bwd_twopass) needs for B samples, total_rows rows and D features on
  * the current device.  Returns 0 for invalid sizes.  The size depends on the
@@ -139,7 +141,8 @@ size_t adaln_bwd_workspace_size(int64_t B, int64_t total_rows, int64_t D, adaln_
  * Outputs must not overlap inputs, each other or the workspace.  With N == 0
  * the call writes zeros to dscale and dshift.  Two launches: a fused row pass
  * (dx plus per-tile column partial sums kept along D) and a deterministic
- * finish that adds each sample's tile partials in ascending tile order.
+ * finish that adds each sample's tile partials in fp64 in an order fixed by
+ * the shape and the device's CU count, and rounds each sum once.
  * Section 2.B, backward bullet.
  */
 adaln_status_t adaln_bwd(const void* dy, const void* x, const void* scale,
@@ -161,6 +164,14 @@ adaln_status_t adaln_bwd(const void* dy, const void* x, const void* scale,
  *
  * Samples may have zero rows.  One kernel launch; each row finds its sample
  * by binary search over the offsets.
+ *
+ * Packed samples of different lengths are the summary's setting: mixed-mode
+ * corpora whose sequence lengths range from still images to long videos
+ * (section 1, problem statement), batched into groups of equal length and
+ * varying batch size by the dual-constraint rule (section 2.A); a packed call
+ * runs such a group, or several, in one launch.  The offsets are clamped to
+ * [0, total_rows] where the kernels read them, so a malformed table gives
+ * wrong results, never an access outside the tensors.
  */
 adaln_status_t adaln_fwd_varlen(const void* x, const void* shift, const void* scale, float eps,
                                 const int64_t* offsets_dev, int64_t B, int64_t total_rows,
@@ -169,10 +180,12 @@ adaln_status_t adaln_fwd_varlen(const void* x, const void* shift, const void* sc
 
 /*
  * adaln_bwd_varlen -- backward of B packed samples (offsets as in
- * adaln_fwd_varlen).  Three launches: a one-workgroup prologue that turns
- * the offsets into a table of row tiles (each inside one sample) in the
- * workspace, the fused row pass, and the deterministic finish.  A sample
- * with zero rows gets zero dscale and dshift.
+ * adaln_fwd_varlen: the summary's mixed-length groups, section 1 and section
+ * 2.A; the per-sample column sums are section 2.B's backward reduction over N,
+ * taken over each sample's own rows).  Three launches: a one-workgroup
+ * prologue that turns the offsets into a table of row tiles (each inside one
+ * sample) in the workspace, the fused row pass, and the deterministic finish.
+ * A sample with zero rows gets zero dscale and dshift.
  */
 adaln_status_t adaln_bwd_varlen(const void* dy, const void* x, const void* scale,
                                 const float* mean, const float* rstd,
@@ -264,10 +277,12 @@ adaln_status_t adaln_bwd_noalloc(const void* dy, const void* x, const void* scal
                                  int64_t B, int64_t N, int64_t D, adaln_dtype_t dtype,
                                  hipStream_t stream, void* dx, void* dscale, void* dshift);
 
-/* Human-readable name of a status code (static storage; never NULL). */
+/* Infrastructure: human-readable name of a status code (static storage;
+ * never NULL; "ADALN_ERR_UNKNOWN" for a value outside adaln_status_t). */
 const char* adaln_status_str(adaln_status_t status);
 
-/* ADALN_ABI_VERSION of the built library. */
+/* Infrastructure: ADALN_ABI_VERSION of the built library, for a caller to
+ * check against the header it was compiled with. */
 int adaln_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,8 +1,18 @@
-"""Throughput regression guard: bench.py on the video, MMDiT and DiT
-workloads must reach at least 85% of the last accepted GB/s on one MI355X
-(box-to-box spread of the same kernels is about 3%).  Each run is bench.py
-itself, in a child process, so the guard times exactly what the bench line
-reports; the line's fields and roofline arithmetic are checked too."""
+"""Throughput guards for bench.py on one MI355X, each run being bench.py
+itself in a child process, so the guard times exactly what the bench line
+reports.
+
+* The video workload under the short warm-up the recorded runs use
+  (--steps 20 --warmup 5): the timed steps then fall in the first few
+  milliseconds of sustained load, when the engine clock sits at 1.6-1.8 GHz
+  instead of 2.4 GHz.  Floor: 5,300 GB/s, the rate the previous kernels
+  reached there, so a return to them fails.
+* The video, MMDiT and DiT workloads after the default >= 100 ms warm-up, at
+  the settled clock: at least 97-98% of the last accepted figures (box-to-box
+  spread of the same kernels is about 1-3%); for video that floor is 5,520
+  GB/s, 69% of the 8 TB/s peak.
+
+The line's fields, roofline arithmetic and ceiling probes are checked too."""
 
 import json
 import os
@@ -15,30 +25,41 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# last accepted bench.py values (GB/s of algorithmic bytes) on MI355X
-ACCEPTED_GBS = {"video_bf16": 5640.0, "mmdit_bf16": 3600.0, "dit_bf16": 3150.0}
-FLOOR = 0.85
+# (config, extra bench.py arguments, floor in GB/s of algorithmic bytes)
+CASES = [
+    ("video_bf16", ["--steps", "20", "--warmup", "5"], 5300.0),
+    ("video_bf16", ["--steps", "50"], 5520.0),
+    ("mmdit_bf16", ["--steps", "50"], 3450.0),
+    ("dit_bf16", ["--steps", "50"], 3050.0),
+]
 
 
-@pytest.mark.parametrize("config", list(ACCEPTED_GBS))
-def test_bench_throughput_floor(config):
-    print(f"[perf] bench.py --config {config}", flush=True)
-    run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--steps", "50",
+@pytest.mark.parametrize("config,extra,floor", CASES,
+                         ids=[f"{c}-{'short' if '--warmup' in e else 'settled'}" for c, e, _ in CASES])
+def test_bench_throughput_floor(config, extra, floor):
+    print(f"[perf] bench.py --config {config} {' '.join(extra)}", flush=True)
+    run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, *extra,
                           "--no-cpu-baseline"], capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert run.returncode == 0, run.stderr[-3000:]
     line = [ln for ln in run.stdout.splitlines() if ln.startswith("{")][-1]
     res = json.loads(line)
-    print(f"  {res['value']} GB/s ({res['pct_of_peak']}% of peak), {res['ms_per_step']} ms/step", flush=True)
-    assert res["value"] >= FLOOR * ACCEPTED_GBS[config], (
-        f"{config}: {res['value']} GB/s is below {FLOOR:.0%} of the accepted {ACCEPTED_GBS[config]} GB/s")
+    print(f"  {res['value']} GB/s ({res['pct_of_peak']}% of peak), {res['ms_per_step']} ms/step, "
+          f"ceiling {res['ceilings']['step_gbs']} GB/s", flush=True)
+    assert res["value"] >= floor, f"{config} {extra}: {res['value']} GB/s is below the floor of {floor} GB/s"
     # the line's contract
     for k, t in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int), ("steps", int),
                  ("warmup", int), ("ms_per_step", float), ("higher_is_better", bool), ("scaling", str),
-                 ("dtype", str), ("data", str), ("config", dict), ("roofline", dict)):
+                 ("dtype", str), ("data", str), ("config", dict), ("roofline", dict), ("ceilings", dict),
+                 ("versions", dict)):
         assert isinstance(res.get(k), t), f"{k}: {res.get(k)!r}"
-    assert "vs_baseline" in res and res["n_gpus"] == 1 and res["steps"] == 50
+    assert "vs_baseline" in res and res["n_gpus"] == 1 and res["steps"] == int(extra[extra.index("--steps") + 1])
+    if "--warmup" in extra:
+        assert res["warmup"] == int(extra[extra.index("--warmup") + 1])
     assert res["config"]["name"] == config and isinstance(res["config"]["workload"], str)
     rf = res["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and 0.0 < rf["frac"] < 1.0
     assert "traffic" in rf
+    c = res["ceilings"]
+    assert 0 < c["copy"]["gbs"] < 8000 and 0 < c["two_to_one"]["gbs"] < 8000
+    assert abs(c["pct_of_copy_ceiling"] - 100 * res["value"] / c["step_gbs"]) < 0.05

@@ -41,7 +41,9 @@ buffers of the workload's own [R, D] size, after the timed region: a copy
 backward row pass's), each the best of a small sweep of launch shapes.
 `step_gbs` is the rate a step would reach if its forward bytes moved at the
 copy rate and its backward bytes at the two-to-one rate, and
-`pct_of_copy_ceiling` is `value` against it.  `versions` records ROCm,
+`pct_of_copy_ceiling` is `value` against it.  Small tensors (DiT's 19 MB)
+are dominated by launch and ramp costs, which the same sweep measures for
+plain streaming as well.  `versions` records ROCm,
 HIP and torch, and `device.compute_partition` the partition mode.
 
 `--bwd twopass` runs the backward through adaln_bwd_twopass instead (dx
@@ -220,7 +222,7 @@ def cpu_baseline(pd, seconds, gpu_rows=None):
     return out
 
 
-PROBE_SHAPES = [(wg, u) for wg in (1, 2, 4) for u in (1, 2, 4, 8)]
+PROBE_SHAPES = [(wg, u) for wg in (1, 2, 4, 8, 16) for u in (1, 2, 4, 8)]
 
 
 def ceilings(adaln, torch, np, runner, nbytes_fwd, nbytes_bwd):

@@ -1207,9 +1207,10 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
   }
 }
 
-// Few samples, at most NARROW_MAX_TILES tiles each: one 256-thread workgroup
-// per (sample, 16-column chunk).  Thread (slice, lane) adds tiles slice,
-// slice + 64, ... (ascending, at most 8) for 4 adjacent columns in fp64; the
+// Few samples: one 256-thread workgroup per (sample, 16-column chunk).  Thread
+// (slice, lane) adds tiles slice, slice + 64, ... (ascending, 8 per round of
+// loads, as many rounds as the sample has tiles) for 4 adjacent columns in
+// fp64; the
 // 64 slice sums are then added in a fixed two-level order (run r adds slices
 // r, r+8, ..., r+56, then the 8 run sums are added in run order), still in
 // fp64, so the only rounding of a column sum is the final one.  320
@@ -1219,7 +1220,6 @@ __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl,
 constexpr int NARROW_LANES = PCOLS / 4;                  // float4 lanes per chunk
 constexpr int NARROW_SLICES = 256 / NARROW_LANES;        // 64
 constexpr int NARROW_PER = 8;                            // tiles per slice
-constexpr int NARROW_MAX_TILES = NARROW_SLICES * NARROW_PER;
 constexpr int NARROW_MAX_SAMPLES = 16;
 
 template <int DT>
@@ -1248,23 +1248,27 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
   const bool col_ok = d < D;          // D % 4 == 0: the lane's 4 columns are all in or all out
   const float* base = partial + pidx(tl.tiles_alloc, 0, 0, cb * PCOLS) + lane * 4;
 
-  float4 vh[PER], vs[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t t = t0 + slice + u * NSLICE;
-    if (col_ok && t < t1) {
-      vh[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS);
-      vs[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS + PCOLS);
-    } else {
-      vh[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      vs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
   double h[4] = {0.0, 0.0, 0.0, 0.0}, sc[4] = {0.0, 0.0, 0.0, 0.0};
+  // PER tiles of the slice per round (their loads issued together); one
+  // round covers up to NARROW_MAX_TILES tiles, more rounds follow in order
+  for (int64_t r0 = t0; r0 < t1; r0 += NSLICE * PER) {
+    float4 vh[PER], vs[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    h[0] += vh[u].x; h[1] += vh[u].y; h[2] += vh[u].z; h[3] += vh[u].w;
-    sc[0] += vs[u].x; sc[1] += vs[u].y; sc[2] += vs[u].z; sc[3] += vs[u].w;
+    for (int u = 0; u < PER; ++u) {
+      const int64_t t = r0 + slice + u * NSLICE;
+      if (col_ok && t < t1) {
+        vh[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS);
+        vs[u] = *reinterpret_cast<const float4*>(base + t * 2 * PCOLS + PCOLS);
+      } else {
+        vh[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        vs[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      h[0] += vh[u].x; h[1] += vh[u].y; h[2] += vh[u].z; h[3] += vh[u].w;
+      sc[0] += vs[u].x; sc[1] += vs[u].y; sc[2] += vs[u].z; sc[3] += vs[u].w;
+    }
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -1591,14 +1595,13 @@ static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
                   : finish_launch<DT>(rm, D, tl, partial, stream, dscale, dshift);
 }
 
-// finish: the narrow kernel for few samples whose tiles fit one workgroup,
-// else one workgroup per (sample, 64 columns)
+// finish: the narrow kernel for few samples (any number of tiles each), else
+// one workgroup per (sample, 64 columns)
 template <int DT>
 static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
                                 const float* partial, hipStream_t stream, void* dscale,
                                 void* dshift) {
-  const int64_t max_tiles_per_sample = (rm.R + tl.tile_rows - 1) / tl.tile_rows;
-  if (D % 4 == 0 && rm.B <= NARROW_MAX_SAMPLES && max_tiles_per_sample <= NARROW_MAX_TILES) {
+  if (D % 4 == 0 && rm.B <= NARROW_MAX_SAMPLES) {
     const int col_blocks = static_cast<int>((D + PCOLS - 1) / PCOLS);
     hipLaunchKernelGGL((finish_narrow_kernel<DT>), dim3(static_cast<unsigned>(rm.B * col_blocks)),
                        dim3(256), 0, stream, partial, rm, tl, static_cast<int>(D), col_blocks,

@@ -6,13 +6,16 @@ Tolerances (the operator's accuracy contract):
             dscale and dshift
   bf16 I/O: max abs error 2e-2 on y and dx; max relative error 1e-2 on
             dscale and dshift
-The relative error of a column sum uses max(|ref|, 1e-2 * rms(ref of that
+The relative error of a column sum uses max(|ref|, 5e-3 * rms(ref of that
 sample)) as denominator: with fp32 statistics and accumulation, a sum of N
 terms carries an absolute error of order u * rms(ref) (u = 2^-24, times a
 small constant for the rounding of xhat and of the running sum) whatever its
-value, so a relative error of 1e-4 can only be asked of sums at least about
-1e-2 * rms(ref) in size; smaller sums (about 1% of a sample's columns) are
-judged on that absolute scale.  Two stricter internal gates are applied as well:
+value, so a relative error of 1e-4 can only be asked of sums above a small
+fraction of rms(ref); smaller sums (well under 1% of a sample's columns) are
+judged on that absolute scale.  The floor comes from a float32 model of the
+kernels' arithmetic (tests/f32_emulation.py, tests/test_tolerance_emulation.py):
+at 1e-3 * rms that model exceeds 1e-4 by up to 40%, at 5e-3 * rms it stays
+within 1e-4 with a margin of 1.5 or more.  Two stricter internal gates are applied as well:
 normwise error max|got-ref| / max|ref| of y and dx at most 1e-2 (bf16) or
 1e-5 (fp32), and fp32 statistics (mean, rstd) within 1e-5 relative to the
 row's scale.
@@ -40,7 +43,7 @@ TOL = {
     "bf16": {"abs": 2e-2, "rel": 1e-2, "norm": 1e-2},
 }
 STAT_TOL = 1e-5
-REL_FLOOR = 1e-2
+REL_FLOOR = 5e-3
 MEAN_ULPS = 4.0
 U32 = 2.0 ** -24
 

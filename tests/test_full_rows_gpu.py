@@ -1,6 +1,7 @@
 """Every row of the full-size workloads against the fp64 oracle.
 
-y, dx, mean and rstd of every row of the DiT, MMDiT and video workloads, and
+y, dx, mean and rstd of every row of the DiT, MMDiT (both streams, and packed
+into one batch) and video workloads, and
 of the fuzz grid's 4,097-row batches, are compared element by element (the
 oracle runs over row chunks), together with every sample's column sums.  The
 persistent forward is also checked in full where each wave carries several
@@ -24,7 +25,7 @@ def _pd(dtype, D, lengths, seed=0, dense=None, **kw):
     return workloads.make_problem_data(p, seed)
 
 
-@pytest.mark.parametrize("name", ["dit_bf16", "mmdit_bf16", "video_bf16"])
+@pytest.mark.parametrize("name", ["dit_bf16", "mmdit_bf16", "mmdit_packed_bf16", "video_bf16"])
 def test_full_size_every_row(name):
     for pd in workloads.make_config(name):
         p = pd.problem

@@ -53,7 +53,8 @@ def test_small_workloads_full_check(name):
 # ---------------------------------------------------------------------------
 # full-size workloads: sampled rows, whole-sample sums
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["dit_bf16", "mmdit_bf16", "video_bf16", "ragged_bf16", "long64k_bf16"])
+@pytest.mark.parametrize("name", ["dit_bf16", "mmdit_bf16", "mmdit_packed_bf16", "video_bf16", "ragged_bf16",
+                                  "long64k_bf16"])
 def test_full_size_workloads_sampled(name):
     for pd in workloads.make_config(name):
         p = pd.problem

@@ -78,3 +78,22 @@ def test_algorithmic_bytes_video():
     p = workloads.CONFIGS["video_bf16"][0]
     b = workloads.algorithmic_bytes(p)
     assert b["fwd"] == 387_243_680 and b["bwd"] == 580_789_920 and b["total"] == 968_033_600
+
+
+def test_packed_workload_is_its_problems_back_to_back():
+    """pack() lays several problems' samples out in order, rows concatenated,
+    each sample keeping its modulation, with the same algorithmic bytes as the
+    separate calls; the packed MMDiT workload is the two MMDiT streams."""
+    a = workloads.make_problem_data(workloads.custom_problem("bf16", 64, [5, 5], outlier_frac=0.1), 1)
+    b = workloads.make_problem_data(workloads.custom_problem("bf16", 64, [9, 9]), 2)
+    pk = workloads.pack([a, b], "packed_test")
+    p = pk.problem
+    assert not p.dense and p.lengths == (5, 5, 9, 9) and p.R == 28 and p.B == 4
+    assert list(pk.offsets) == [0, 5, 10, 19, 28]
+    for k in ("x", "dy", "shift", "scale"):
+        assert np.array_equal(getattr(pk, k), np.concatenate([getattr(a, k), getattr(b, k)])), k
+    total = sum(workloads.algorithmic_bytes(q.problem)["total"] for q in (a, b))
+    assert workloads.algorithmic_bytes(p)["total"] == total
+    assert workloads.PACKED_CONFIGS["mmdit_packed_bf16"] == "mmdit_bf16"
+    assert [q.lengths for q in workloads.CONFIGS["mmdit_bf16"]] == [(512, 512), (4096, 4096)]
+    assert "mmdit_packed_bf16" in workloads.config_names()

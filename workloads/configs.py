@@ -17,6 +17,8 @@ below are seeded Gaussian stand-ins of the same shapes):
                x~N(0,1) with 1% of each stream's rows multiplied by 20;
                dy~N(0,1e-2); each stream has its own shift/scale
   video_bf16   B=1, N=18900, D=5120, bf16; x~N(0,1); dy~N(0,1e-3)
+  mmdit_packed_bf16  the two MMDiT streams' data as one packed batch of four
+               samples (512, 512, 4096, 4096 rows), one call per direction
   ragged_bf16  D=3072, bf16, packed rows of 277 samples: 256 samples of 256
                rows, 16 of 4096, 4 of 16384, 1 of 32760 (bucket sizes from the
                page's dual-constraint rule with M_mem=65536, M_comp=2^30, p=2);
@@ -141,6 +143,12 @@ CONFIGS = {
 CONFIG_SEEDS = {"tiny_fp32": 1, "dit_bf16": 2, "mmdit_bf16": 3, "video_bf16": 4, "ragged_bf16": 5,
                 "long64k_bf16": 6}
 
+# Workloads made by packing another workload's problems back to back into one
+# packed batch (same drawn data, one call per direction instead of one per
+# problem): the MMDiT text and image streams as four samples of 512, 512,
+# 4096 and 4096 rows, each with its own modulation.
+PACKED_CONFIGS = {"mmdit_packed_bf16": "mmdit_bf16"}
+
 
 # --------------------------------------------------------------------------
 # encoding
@@ -249,8 +257,29 @@ def make_problem_data(problem: Problem, seed: int) -> ProblemData:
     )
 
 
+def pack(pds: list, name: str) -> ProblemData:
+    """Several problems' data (same D and dtype) as one packed batch: their
+    samples in order, rows concatenated, each sample keeping its modulation."""
+    p0 = pds[0].problem
+    assert all(pd.problem.D == p0.D and pd.problem.dtype == p0.dtype for pd in pds)
+    lengths = tuple(n for pd in pds for n in pd.problem.lengths)
+    problem = Problem(name, p0.dtype, p0.D, lengths, False, dy_sigma=p0.dy_sigma, eps=p0.eps,
+                      outlier_frac=p0.outlier_frac, outlier_gain=p0.outlier_gain, mod_sigma=p0.mod_sigma)
+    offsets = np.zeros(len(lengths) + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    cat = lambda k: np.concatenate([getattr(pd, k) for pd in pds], axis=0)
+    return ProblemData(problem=problem, x=cat("x"), shift=cat("shift"), scale=cat("scale"), dy=cat("dy"),
+                       offsets=offsets, meta={"packed_from": [pd.problem.name for pd in pds]})
+
+
+def config_names() -> list:
+    return list(CONFIGS) + list(PACKED_CONFIGS)
+
+
 def make_config(name: str, seed: int | None = None) -> list:
     """All problems of a named workload, each with its own derived seed."""
+    if name in PACKED_CONFIGS:
+        return [pack(make_config(PACKED_CONFIGS[name], seed), name)]
     base = CONFIG_SEEDS[name] if seed is None else seed
     return [make_problem_data(p, base * 1000 + i) for i, p in enumerate(CONFIGS[name])]
 

@@ -1250,7 +1250,7 @@ finish_narrow_kernel(const float* __restrict__ partial, RowMap rm, Tiling tl, in
 
   double h[4] = {0.0, 0.0, 0.0, 0.0}, sc[4] = {0.0, 0.0, 0.0, 0.0};
   // PER tiles of the slice per round (their loads issued together); one
-  // round covers up to NARROW_MAX_TILES tiles, more rounds follow in order
+  // round covers NSLICE * PER = 512 tiles, more rounds follow in order
   for (int64_t r0 = t0; r0 < t1; r0 += NSLICE * PER) {
     float4 vh[PER], vs[PER];
 #pragma unroll

@@ -344,31 +344,97 @@ __device__ __forceinline__ int64_t sample_of_row(const RowMap& rm, int64_t row) 
   return lo;
 }
 
-// Rows of tile t: sample b, rows first + m*step for m in [0, count).
-// Sample b's rows are split over its tiles either in contiguous runs of
-// tile_rows rows (step 1) or, with tl.interleave, round-robin (tile k of the
-// sample takes rows k, k + tiles, k + 2*tiles, ...), which keeps the rows in
-// flight across the chip inside a narrow moving window.
-__device__ __forceinline__ void tile_rows_of(const RowMap& rm, const Tiling& tl, int64_t t,
+// Packed batches of at most VARLEN_WAVE_MAX_B samples need no tile table in
+// memory (and no prologue launch): any wave rebuilds it from the offsets.
+// Lane i holds sample i's tile count (ceil of its clamped row count over
+// tile_rows); an inclusive prefix sum over the wave gives every sample's tile
+// range [excl, incl), both capped at tiles_alloc exactly as the prologue caps
+// the table it writes, so both ways number the tiles identically.  Every lane
+// of the wave must take part.
+constexpr int VARLEN_WAVE_MAX_B = 64;
+
+struct WaveTiles {
+  int64_t excl, incl;   // this lane's sample: tiles [excl, incl)
+};
+
+// v from lane `lane` (wave-uniform) as a wave-uniform value, so that what is
+// derived from it stays in scalar registers.
+__device__ __forceinline__ int64_t lane_value(int64_t v, int lane) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+  const int32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), lane);
+  return (static_cast<int64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ WaveTiles wave_tile_table(const RowMap& rm, const Tiling& tl) {
+  const int lane = threadIdx.x & 63;
+  int64_t cnt = 0;
+  if (lane < rm.B) {
+    const int64_t n = clamped_span(rm.offsets[lane], rm.offsets[lane + 1], rm.R).n;
+    cnt = n > 0 ? (n + tl.tile_rows - 1) / tl.tile_rows : 0;
+  }
+  int64_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  return WaveTiles{min(incl - cnt, tl.tiles_alloc), min(incl, tl.tiles_alloc)};
+}
+
+// Sample b of packed tile t (the largest b whose first tile is <= t) and its
+// tiles [t0, t1); false when t is at or past the last tile (a spare
+// workgroup of the packed grid).  Table in memory, or rebuilt by the wave.
+__device__ __forceinline__ bool varlen_tile_sample(const RowMap& rm, const Tiling& tl, int64_t t,
+                                                   int64_t& b, int64_t& t0, int64_t& t1) {
+  if (tl.tile_start == nullptr) {
+    const WaveTiles w = wave_tile_table(rm, tl);
+    const int lane = threadIdx.x & 63;
+    if (t >= lane_value(w.incl, 63)) return false;   // lanes >= B add nothing: lane 63 has the total
+    const unsigned long long below = __ballot(lane < rm.B && w.excl <= t);   // lane 0 always
+    const int bl = 63 - __clzll(static_cast<long long>(below));
+    b = bl;
+    t0 = lane_value(w.excl, bl);
+    t1 = lane_value(w.incl, bl);
+    return true;
+  }
+  if (t >= tl.tile_start[rm.B]) return false;
+  int64_t lo = 0, hi = rm.B;
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (tl.tile_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  b = lo;
+  t0 = tl.tile_start[b];
+  t1 = tl.tile_start[b + 1];
+  return true;
+}
+
+// Rows of tile t: sample b, rows first + m*step for m in [0, count); false
+// for a spare workgroup of the packed grid (past the last tile), which then
+// has nothing to do.  Sample b's rows are split over its tiles either in
+// contiguous runs of tile_rows rows (step 1) or, with tl.interleave,
+// round-robin (tile k of the sample takes rows k, k + tiles, k + 2*tiles,
+// ...), which keeps the rows in flight across the chip inside a narrow
+// moving window.  Every thread of the workgroup calls this (the packed
+// lookup may use wave-wide operations).  PACKED: the batch has an offsets
+// table (a compile-time choice, so that the dense kernels carry none of the
+// packed lookup's registers).
+template <bool PACKED>
+__device__ __forceinline__ bool tile_rows_of(const RowMap& rm, const Tiling& tl, int64_t t,
                                              int64_t& b, int64_t& first, int64_t& step,
                                              int64_t& count) {
   int64_t k, tiles, lo_row, n;
-  if (rm.offsets == nullptr) {
+  if constexpr (!PACKED) {
     tiles = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
     b = t / tiles;
     k = t - b * tiles;
     lo_row = b * rm.N;
     n = rm.N;
   } else {
-    // largest b with tile_start[b] <= t
-    int64_t lo = 0, hi = rm.B;
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (tl.tile_start[mid] <= t) lo = mid; else hi = mid;
-    }
-    b = lo;
-    k = t - tl.tile_start[b];
-    tiles = tl.tile_start[b + 1] - tl.tile_start[b];
+    int64_t t0, t1;
+    if (!varlen_tile_sample(rm, tl, t, b, t0, t1)) return false;
+    k = t - t0;
+    tiles = t1 - t0;
     const RowSpan sp = clamped_span(rm.offsets[b], rm.offsets[b + 1], rm.R);
     lo_row = sp.lo;
     n = sp.n;
@@ -382,6 +448,7 @@ __device__ __forceinline__ void tile_rows_of(const RowMap& rm, const Tiling& tl,
     step = 1;
     count = min(tl.tile_rows, n - k * tl.tile_rows);
   }
+  return true;
 }
 
 // Tile partials are chunk-major (PCOLS columns per chunk, see
@@ -656,7 +723,7 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 // workgroup holds several slots, [slots][D] floats for the slot combine.
 // COLS = false compiles out the column partials: dx only (the first pass of
 // the two-pass backward).
-template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool COLS = true>
+template <int DT, int VPT, int RIF, int NTMAX = VEC_MAX_NT, bool COLS = true, bool PACKED = false>
 __global__ void __launch_bounds__(NTMAX)
 bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
                const uint4* __restrict__ scale, const float* __restrict__ mean,
@@ -667,9 +734,8 @@ bwd_vec_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   extern __shared__ float2 lds_f2[];
 
   const int64_t t = blockIdx.x;
-  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
   int64_t b, first, step, count;
-  tile_rows_of(rm, tl, t, b, first, step, count);
+  if (!tile_rows_of<PACKED>(rm, tl, t, b, first, step, count)) return;   // spare packed workgroup
 
   const int tid = threadIdx.x;
   const int nslots = blockDim.x / lpr;
@@ -888,7 +954,7 @@ __device__ __forceinline__ float sum_to_last_lane(float v) {
 
 constexpr int ROW_MAX_WAVES = VEC_MAX_NT / 64;
 
-template <int DT, int VPT, bool COLS = true>
+template <int DT, int VPT, bool COLS = true, bool PACKED = false>
 __global__ void __launch_bounds__(VEC_MAX_NT)
 bwd_row_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
                const uint4* __restrict__ scale, const float* __restrict__ mean,
@@ -902,9 +968,8 @@ bwd_row_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   __shared__ float2 red[2][ROW_MAX_WAVES];
 
   const int64_t t = blockIdx.x;
-  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
   int64_t b, first, step, count;
-  tile_rows_of(rm, tl, t, b, first, step, count);
+  if (!tile_rows_of<PACKED>(rm, tl, t, b, first, step, count)) return;   // spare packed workgroup
   const int lane = threadIdx.x;
   const int wave = lane >> 6;
   const float inv_d = 1.0f / static_cast<float>(D);
@@ -1028,9 +1093,8 @@ dtile_cols_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ x,
   constexpr int EPV = E::EPV;
   __shared__ float red[DT_WAVES - 1][64][2 * EPV];
   const int64_t t = blockIdx.x;
-  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;   // spare varlen workgroup
   int64_t b, first, step, count;
-  tile_rows_of(rm, tl, t, b, first, step, count);
+  if (!tile_rows_of<false>(rm, tl, t, b, first, step, count)) return;   // dense batches only
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int v = blockIdx.y * 64 + lane;
@@ -1142,7 +1206,7 @@ fwd_gen_kernel(const void* __restrict__ x, const void* __restrict__ shift,
 
 // One workgroup per tile; column partials accumulate in the tile's slice of
 // `partial`, each column owned by one thread for the whole tile.
-template <int DT>
+template <int DT, bool PACKED>
 __global__ void __launch_bounds__(GEN_NT)
 bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
                const void* __restrict__ scale, const float* __restrict__ mean,
@@ -1151,9 +1215,8 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
   using E = Elem<DT>;
   __shared__ float red[4][GEN_NT / 64];
   const int64_t t = blockIdx.x;
-  if (rm.offsets != nullptr && t >= tl.tile_start[rm.B]) return;
   int64_t b, first, step, count;
-  tile_rows_of(rm, tl, t, b, first, step, count);
+  if (!tile_rows_of<PACKED>(rm, tl, t, b, first, step, count)) return;   // spare packed workgroup
   const int64_t TA = tl.tiles_alloc;
   for (int d = threadIdx.x; d < D; d += GEN_NT) {
     partial[pidx(TA, t, 0, d)] = 0.f;
@@ -1196,12 +1259,17 @@ bwd_gen_kernel(const void* __restrict__ dy, const void* __restrict__ x,
 // hand-off inside one kernel (46 us: each workgroup's device-scope release
 // fence writes back its XCD's L2); groups-then-samples in two kernels (13 us).
 
-// Tiles [t0, t1) of sample b.
+// Tiles [t0, t1) of sample b (b uniform over the workgroup; every thread
+// calls this).
 __device__ __forceinline__ void sample_tiles(const RowMap& rm, const Tiling& tl, int64_t b,
                                              int64_t& t0, int64_t& t1) {
   if (rm.offsets == nullptr) {
     const int64_t tps = (rm.N + tl.tile_rows - 1) / tl.tile_rows;
     t0 = b * tps; t1 = t0 + tps;
+  } else if (tl.tile_start == nullptr) {
+    const WaveTiles w = wave_tile_table(rm, tl);
+    t0 = lane_value(w.excl, static_cast<int>(b));
+    t1 = lane_value(w.incl, static_cast<int>(b));
   } else {
     t0 = tl.tile_start[b]; t1 = tl.tile_start[b + 1];
   }
@@ -1437,10 +1505,19 @@ static hipError_t bwd_row_launch(const void* dy, const void* x, const void* scal
                                  const float* mean, const float* rstd, const RowMap& rm,
                                  int64_t D, const VecPlan& vp, const Tiling& tl, float* partial,
                                  hipStream_t stream, void* dx) {
-  hipLaunchKernelGGL((bwd_row_kernel<DT, VPT, COLS>), dim3(static_cast<unsigned>(tl.tiles_max)),
-                     dim3(vp.lpr), 0, stream, static_cast<const uint4*>(dy),
-                     static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
-                     tl, static_cast<int>(D), partial, static_cast<uint4*>(dx));
+#define ADALN_ROW_LAUNCH(P)                                                                        \
+  hipLaunchKernelGGL((bwd_row_kernel<DT, VPT, COLS, P>), dim3(static_cast<unsigned>(tl.tiles_max)), \
+                     dim3(vp.lpr), 0, stream, static_cast<const uint4*>(dy),                      \
+                     static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm, \
+                     tl, static_cast<int>(D), partial, static_cast<uint4*>(dx))
+  if constexpr (COLS) {        // dx-only passes (the two-pass backward) take dense batches only
+    if (rm.offsets != nullptr) {
+      ADALN_ROW_LAUNCH(true);
+      return hipGetLastError();
+    }
+  }
+  ADALN_ROW_LAUNCH(false);
+#undef ADALN_ROW_LAUNCH
   return hipGetLastError();
 }
 
@@ -1453,10 +1530,20 @@ static hipError_t bwd_vec_launch(const void* dy, const void* x, const void* scal
   constexpr int RIF = BWD_RIF;
   const int V = static_cast<int>(D / EPV);
   const size_t lds = vec_lds_bytes(vp, D, true);
-  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF, VEC_MAX_NT, COLS>), dim3(static_cast<unsigned>(tl.tiles_max)),
-                     dim3(vp.nt), lds, stream, static_cast<const uint4*>(dy),
-                     static_cast<const uint4*>(x), static_cast<const uint4*>(scale), mean, rstd, rm,
-                     tl, V, static_cast<int>(D), vp.lpr, partial, static_cast<uint4*>(dx));
+#define ADALN_VEC_LAUNCH(P)                                                                         \
+  hipLaunchKernelGGL((bwd_vec_kernel<DT, VPT, RIF, VEC_MAX_NT, COLS, P>),                          \
+                     dim3(static_cast<unsigned>(tl.tiles_max)), dim3(vp.nt), lds, stream,          \
+                     static_cast<const uint4*>(dy), static_cast<const uint4*>(x),                  \
+                     static_cast<const uint4*>(scale), mean, rstd, rm, tl, V, static_cast<int>(D), \
+                     vp.lpr, partial, static_cast<uint4*>(dx))
+  if constexpr (COLS) {        // dx-only passes (the two-pass backward) take dense batches only
+    if (rm.offsets != nullptr) {
+      ADALN_VEC_LAUNCH(true);
+      return hipGetLastError();
+    }
+  }
+  ADALN_VEC_LAUNCH(false);
+#undef ADALN_VEC_LAUNCH
   return hipGetLastError();
 }
 
@@ -1564,8 +1651,14 @@ static hipError_t bwd_gen_launch(const void* dy, const void* x, const void* scal
                                  const float* mean, const float* rstd, const RowMap& rm,
                                  int64_t D, const Tiling& tl, float* partial, hipStream_t stream,
                                  void* dx) {
-  hipLaunchKernelGGL((bwd_gen_kernel<DT>), dim3(static_cast<unsigned>(tl.tiles_max)), dim3(GEN_NT),
-                     0, stream, dy, x, scale, mean, rstd, rm, tl, static_cast<int>(D), partial, dx);
+  if (rm.offsets != nullptr)
+    hipLaunchKernelGGL((bwd_gen_kernel<DT, true>), dim3(static_cast<unsigned>(tl.tiles_max)),
+                       dim3(GEN_NT), 0, stream, dy, x, scale, mean, rstd, rm, tl,
+                       static_cast<int>(D), partial, dx);
+  else
+    hipLaunchKernelGGL((bwd_gen_kernel<DT, false>), dim3(static_cast<unsigned>(tl.tiles_max)),
+                       dim3(GEN_NT), 0, stream, dy, x, scale, mean, rstd, rm, tl,
+                       static_cast<int>(D), partial, dx);
   return hipGetLastError();
 }
 
@@ -1574,18 +1667,29 @@ static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
                                 const float* partial, hipStream_t stream, void* dscale,
                                 void* dshift);
 
+// The packed batch's tile table: batches of at most VARLEN_WAVE_MAX_B
+// samples rebuild it wave by wave inside the kernels (tile_start = nullptr
+// tells them so), larger ones get it from the prologue kernel.
+static hipError_t varlen_tile_table(const RowMap& rm, Tiling& tl, hipStream_t stream) {
+  if (rm.offsets == nullptr) return hipSuccess;
+  if (rm.B <= VARLEN_WAVE_MAX_B) {
+    tl.tile_start = nullptr;
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
+                     rm.R, tl.tile_rows, tl.tiles_alloc, tl.tile_start);
+  return hipGetLastError();
+}
+
 template <int DT>
 static hipError_t bwd_dispatch(const void* dy, const void* x, const void* scale,
                                const float* mean, const float* rstd, const RowMap& rm, int64_t D,
-                               bool vec, const VecPlan& vp, const Tiling& tl, float* partial,
+                               bool vec, const VecPlan& vp, const Tiling& tl_in, float* partial,
                                hipStream_t stream, void* dx, void* dscale, void* dshift,
                                bool sums_f32) {
-  hipError_t e = hipSuccess;
-  if (rm.offsets != nullptr) {
-    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       rm.R, tl.tile_rows, tl.tiles_alloc, tl.tile_start);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  Tiling tl = tl_in;
+  hipError_t e = varlen_tile_table(rm, tl, stream);
+  if (e != hipSuccess) return e;
   if (rm.R > 0 && tl.tiles_max > 0) {
     e = vec ? bwd_rows<DT, true>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx)
             : bwd_gen_launch<DT>(dy, x, scale, mean, rstd, rm, D, tl, partial, stream, dx);
@@ -1620,15 +1724,12 @@ static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
 template <int DT>
 static hipError_t bwd_twopass_dispatch(const void* dy, const void* x, const void* scale,
                                        const float* mean, const float* rstd, const RowMap& rm,
-                                       int64_t D, const VecPlan& vp, const Tiling& tl,
+                                       int64_t D, const VecPlan& vp, const Tiling& tl_in,
                                        float* partial, hipStream_t stream, void* dx,
                                        void* dscale, void* dshift) {
+  if (rm.offsets != nullptr) return hipErrorInvalidValue;   // dense batches only
+  const Tiling& tl = tl_in;
   hipError_t e = hipSuccess;
-  if (rm.offsets != nullptr) {
-    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(PRO_NT), 0, stream, rm.offsets, rm.B,
-                       rm.R, tl.tile_rows, tl.tiles_alloc, tl.tile_start);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if (rm.R > 0 && tl.tiles_max > 0) {
     e = bwd_rows<DT, false>(dy, x, scale, mean, rstd, rm, D, vp, tl, partial, stream, dx);
     if (e != hipSuccess) return e;

@@ -386,8 +386,65 @@ static void test_offset_clamp() {
   }
 }
 
+// Packed batches of at most 64 samples number their tiles without the
+// prologue's table: a wave holds each sample's capped exclusive prefix
+// (lane i: sample i) and a tile's sample is the highest lane whose prefix is
+// <= t (a ballot), a tile at or past the capped total being spare.  That
+// lookup must agree with the binary search over the prologue's table for
+// every tile, empty and malformed samples included.
+static void test_wave_tile_lookup() {
+  const int64_t R = 5000, D = 256;
+  const int cus = 256;
+  std::vector<std::vector<int64_t>> tables = {
+      {0, 5000}, {0, 0, 5000}, {0, 5000, 5000}, {0, 1, 2, 3, 4}, {0, 100, 100, 100, 4000, 5000},
+      {-50, 400, 9000}, {0, 900, 100, 1000}, {0, 5000, 0, 5000, 0, 5000}, {INT64_MIN, INT64_MAX}};
+  uint64_t seed = 12345;
+  auto next = [&seed]() { seed = seed * 6364136223846793005ull + 1442695040888963407ull; return seed >> 33; };
+  for (int B : {1, 2, 5, 17, 63, 64}) {
+    std::vector<int64_t> o(B + 1, 0);
+    for (int b = 1; b <= B; ++b) o[b] = o[b - 1] + static_cast<int64_t>(next() % 3 == 0 ? 0 : next() % 300);
+    tables.push_back(o);
+  }
+  for (const auto& o : tables) {
+    const int64_t B = static_cast<int64_t>(o.size()) - 1;
+    const adaln::WorkspaceLayout w = adaln::bwd_workspace_layout(B, R, D, cus, true, 0);
+    const int64_t TA = w.tiles_alloc;
+    // the prologue's table
+    std::vector<int64_t> start(B + 1);
+    int64_t carry = 0;
+    std::vector<int64_t> excl(B), incl(B);
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t n = adaln::clamped_span(o[b], o[b + 1], R).n;
+      const int64_t cnt = n > 0 ? (n + w.tile_rows - 1) / w.tile_rows : 0;
+      start[b] = carry < TA ? carry : TA;
+      excl[b] = start[b];
+      carry += cnt;
+      incl[b] = carry < TA ? carry : TA;
+    }
+    start[B] = carry < TA ? carry : TA;
+    bool ok = true;
+    for (int64_t t = 0; t < TA + 3; ++t) {
+      const bool spare_table = t >= start[B];
+      const bool spare_wave = t >= incl[B - 1];
+      ok = ok && spare_table == spare_wave;
+      if (spare_table) continue;
+      int64_t lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (start[mid] <= t) lo = mid; else hi = mid;
+      }
+      int64_t bw = 0;
+      for (int64_t i = 0; i < B; ++i)
+        if (excl[i] <= t) bw = i;
+      ok = ok && bw == lo && excl[bw] == start[lo] && incl[bw] == start[lo + 1];
+    }
+    EXPECT(ok, "wave tile lookup differs from the prologue table (B %lld)", (long long)B);
+  }
+}
+
 int main() {
   test_offset_clamp();
+  test_wave_tile_lookup();
   test_plans();
   test_forward();
   test_forward_varlen();

@@ -122,6 +122,24 @@ def test_many_packed_samples(dtype, D):
     check_all(pd, run_gpu(pd))
 
 
+# Packed batches of up to 64 samples number their tiles inside the kernels
+# (one wave rebuilds the table from the offsets); from 65 on a prologue kernel
+# writes it.  Both sides of that switch, with empty samples in the first and
+# the last lane and a ragged mix of lengths.
+@pytest.mark.parametrize("dtype,D,B", [("bf16", 3072, 64), ("bf16", 3072, 65), ("f32", 128, 64),
+                                       ("f32", 128, 65), ("bf16", 1152, 1)])
+def test_packed_tile_table_switch(dtype, D, B):
+    g = np.random.Generator(np.random.PCG64(23))
+    lengths = g.integers(1, 300, size=B).tolist()
+    if B > 1:
+        lengths[0] = 0
+        lengths[min(63, B - 1)] = 0
+        lengths[B // 2] = 1500
+    pd = _pd(dtype, D, lengths, seed=24, dense=False)
+    say(f"[tile-table] {dtype} D={D} B={B} R={pd.problem.R}")
+    check_all(pd, run_gpu(pd))
+
+
 # Many short samples through the dense entry points: B far above the narrow
 # finish's 16 samples, tiles of a few rows each.
 @pytest.mark.parametrize("dtype,D,B,N", [("bf16", 1152, 3000, 3), ("f32", 128, 2049, 5)])

@@ -55,6 +55,11 @@ count stays that of the I/O-typed sums, 2*B*D*s fewer bytes than written).
 `--cost-sweep` does the shape benchmarking of the batch scheduler instead
 (see cost_sweep) and prints its own JSON line.
 
+`--clock-trace` runs the same schedule (priming, warm-up, K steps) with the
+engine clock sampled beside it by the library's clock probe on a second
+stream, and prints the clock over time and per step instead of a throughput
+line (see clock_trace).
+
 `--impl torch` runs the unfused chain an eager framework executes instead
 (LayerNorm without affine, multiply by 1 + scale, add shift; backward by
 autograd), on the same resident copies, for context.  Every line reports
@@ -102,6 +107,13 @@ def parse():
     ap.add_argument("--cost-sweep", action="store_true",
                     help="time a synthetic per-group step over (B, S), fit step = a + b*B*S^p with "
                          "adaln_cost_fit and compare equal-token and dual-constraint grouping")
+    ap.add_argument("--clock-trace", action="store_true",
+                    help="sample the engine clock beside the bench's schedule (diagnostic; prints its own line)")
+    ap.add_argument("--clock-samples", type=int, default=20000,
+                    help="most clock samples --clock-trace takes")
+    ap.add_argument("--clock-per-step", type=int, default=4,
+                    help="clock samples queued with each step for --clock-trace (keep their total "
+                         "time near the step's)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -522,6 +534,9 @@ def main():
     nbytes = {k: sum(workloads.algorithmic_bytes(r.p)[k] for r in runners) for k in ("fwd", "bwd", "total")}
     rows = sum(r.p.R for r in runners)
     main_r = max(runners, key=lambda r: r.p.R * r.p.D)     # the roofline reports its backward
+    if args.clock_trace:
+        clock_trace(args, runners, adaln, torch, np)
+        return
 
     for r in runners:
         r.prime()
@@ -674,6 +689,113 @@ def main():
             def gpu_rows(lo, hi):
                 return host64(s0["y"][lo:hi]), host64(s0["dx"][lo:hi]), host64(s0["rstd"][lo:hi])
         out["cpu_baseline"] = cpu_baseline(pd, args.cpu_seconds, gpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+CLOCK_ITERS = 4000        # fma chain of one clock sample
+
+
+def clock_trace(args, runners, adaln, torch, np):
+    """The bench's schedule -- priming, the warm-up (W steps, or batches of ten
+    until --warmup-ms have passed), K steps -- with the engine clock sampled
+    beside it.  A second stream runs single-wave clock probes back to back
+    (each times a chain of dependent fmas in shader-clock cycles and in
+    wall-clock ticks), and a timestamp on the launch stream before every step
+    puts the steps on the same wall clock.  Prints one JSON line: clock
+    samples over time, each step's duration, and the mean clock over the
+    warm-up and over the K steps.  Diagnostic only: the probes hold one wave
+    slot, and no throughput is reported from this run."""
+    khz = adaln.adaln_probe_wall_clock_khz()
+    if khz <= 0:
+        raise SystemExit("the device does not report its wall-clock rate")
+    n_probe = max(256, args.clock_samples)
+    probe = torch.zeros(3 * n_probe, dtype=torch.int64, device="cuda")
+    cap = 4 + (args.warmup if args.warmup is not None else 100000) + args.steps
+    marks = torch.zeros(cap, dtype=torch.int64, device="cuda")
+    phase = []                                   # phase of the step after each mark
+    side = torch.cuda.Stream()
+    fed = [0]
+
+    def feed(n):
+        # clock samples queued on the side stream as the schedule is queued,
+        # so that they run beside it rather than all before it
+        for _ in range(min(n, n_probe - fed[0])):
+            adaln.adaln_probe_clock(probe, fed[0], CLOCK_ITERS, stream=side)
+            fed[0] += 1
+
+    def mark(what):
+        adaln.adaln_probe_mark(marks, len(phase))
+        phase.append(what)
+        feed(args.clock_per_step)
+
+    torch.cuda.synchronize()
+    feed(64)                                     # the idle clock before the schedule
+    mark("prime")
+    for r in runners:
+        r.prime()
+    k = 0
+    if args.warmup is not None:
+        for k in range(args.warmup):
+            mark("warmup")
+            for r in runners:
+                r.step(k)
+    else:
+        t_w = None
+        while (t_w is None or k < 20 or time.perf_counter() - t_w < args.warmup_ms * 1e-3) and len(phase) + 12 + args.steps < cap:
+            for _ in range(10):
+                mark("warmup")
+                for r in runners:
+                    r.step(k)
+                k += 1
+            torch.cuda.synchronize()
+            if t_w is None:
+                t_w = time.perf_counter()
+    for k in range(args.steps):
+        mark("timed")
+        for r in runners:
+            r.step(k)
+    mark("end")
+    feed(64)                                     # and after it
+    torch.cuda.synchronize()
+
+    m = marks.cpu().numpy()[:len(phase)].astype(np.int64)
+    pr = probe.cpu().numpy().reshape(-1, 3).astype(np.int64)
+    t0 = m[0]
+    ms = lambda ticks: ticks * 1.0 / khz                  # wall-clock ticks -> ms
+    ok = pr[:, 2] > 0
+    t_s = ms(pr[ok, 0] - t0)
+    mhz = pr[ok, 1] / pr[ok, 2] * khz / 1e3
+    ph = np.array(phase)
+    t_mark = ms(m - t0)
+    step_us = np.diff(t_mark) * 1e3
+    w_idx = np.where(ph[:-1] == "warmup")[0]
+    t_idx = np.where(ph[:-1] == "timed")[0]
+    t_start = t_mark[t_idx[0]] if len(t_idx) else t_mark[-1]
+    w_start = t_mark[w_idx[0]] if len(w_idx) else t_start
+
+    def mean_in(lo, hi):
+        sel = (t_s >= lo) & (t_s < hi)
+        return (round(float(mhz[sel].mean()), 1), round(float(mhz[sel].min()), 1), int(sel.sum())) if sel.any() else (None, None, 0)
+
+    keep = (t_s >= -1.0) & (t_s <= t_mark[-1] + 1.0)
+    idx = np.where(keep)[0]
+    if len(idx) > 600:
+        idx = idx[:: int(np.ceil(len(idx) / 600))]
+    wm, wmin, wn = mean_in(w_start, t_start)
+    tm, tmin, tn = mean_in(t_start, t_mark[-1])
+    out = {"clock_trace": {
+        "config": args.config, "steps": args.steps, "warmup": int(len(w_idx)),
+        "wall_clock_khz": int(khz), "probe_iters": CLOCK_ITERS,
+        "probe_us": round(float(np.median(pr[ok, 2])) / khz * 1e3, 2),
+        "idle_mhz": round(float(np.median(mhz[t_s < 0])), 1) if (t_s < 0).any() else None,
+        "prime_ms": round(float(w_start), 3),
+        "warmup_mhz": {"mean": wm, "min": wmin, "samples": wn},
+        "timed_mhz": {"mean": tm, "min": tmin, "samples": tn},
+        "timed_start_ms": round(float(t_start), 3), "end_ms": round(float(t_mark[-1]), 3),
+        "timed_step_us": [round(float(v), 1) for v in step_us[t_idx]],
+        "warmup_step_us": [round(float(v), 1) for v in step_us[w_idx]][:50],
+        "samples_ms_mhz": [[round(float(t_s[i]), 3), round(float(mhz[i]), 0)] for i in idx],
+    }}
     print(json.dumps(out), flush=True)
 
 

@@ -4,7 +4,7 @@ The operator runs in hand-written HIP kernels behind the C ABI declared in
 include/adaln.h; this package holds those sources (csrc/), the build step and
 a ctypes binding whose functions carry the C entry points' names.  The same
 library carries the host-side batch scheduler of include/adaln_sched.h and
-the streaming ceiling probes of include/adaln_probe.h.
+the streaming ceiling and engine-clock probes of include/adaln_probe.h.
 """
 from ._lib import (  # noqa: F401
     EXPORTED,
@@ -21,8 +21,11 @@ from ._lib import (  # noqa: F401
     adaln_fwd,
     adaln_fwd_varlen,
     adaln_load_cv,
+    adaln_probe_clock,
+    adaln_probe_mark,
     adaln_probe_read_out_bytes,
     adaln_probe_stream,
+    adaln_probe_wall_clock_khz,
     adaln_sched_batch_size,
     adaln_sched_plan,
     adaln_status_str,

@@ -46,6 +46,9 @@ EXPORTED = (
     "adaln_load_cv",
     "adaln_probe_stream",
     "adaln_probe_read_out_bytes",
+    "adaln_probe_clock",
+    "adaln_probe_mark",
+    "adaln_probe_wall_clock_khz",
 )
 
 
@@ -109,6 +112,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.adaln_probe_stream.restype = ctypes.c_int
     lib.adaln_probe_read_out_bytes.argtypes = [ctypes.c_int]
     lib.adaln_probe_read_out_bytes.restype = ctypes.c_size_t
+    lib.adaln_probe_clock.argtypes = [_P, _I64, _I64, ctypes.c_int, _P]
+    lib.adaln_probe_clock.restype = ctypes.c_int
+    lib.adaln_probe_mark.argtypes = [_P, _I64, _I64, _P]
+    lib.adaln_probe_mark.restype = ctypes.c_int
+    lib.adaln_probe_wall_clock_khz.argtypes = []
+    lib.adaln_probe_wall_clock_khz.restype = _I64
     _lib = lib
     return lib
 
@@ -527,3 +536,34 @@ def adaln_probe_stream(mode: str, a, b, out, wg_per_cu: int, unroll: int, nbytes
     st = _on(dev, lib.adaln_probe_stream, code, _ptr(a), _ptr(b), _ptr(out), int(nbytes), int(wg_per_cu),
              int(unroll), _stream(dev, stream))
     _raise("adaln_probe_stream", st)
+
+
+def _slots(out, per):
+    """Slots of an int64 device tensor holding `per` uint64 values each."""
+    if out.dtype != torch.int64 or not out.is_contiguous() or out.numel() < per:
+        raise ValueError("probe output must be a contiguous int64 tensor")
+    return out.numel() // per
+
+
+def adaln_probe_clock(out, slot: int, iters: int, stream=None):
+    """One engine-clock sample into out[3*slot : 3*slot+3] (int64 device
+    tensor): wall clock at the start, shader-clock cycles, wall-clock ticks."""
+    dev = _check_dev(out)
+    lib = load_library()
+    st = _on(dev, lib.adaln_probe_clock, _ptr(out), _slots(out, 3), int(slot), int(iters), _stream(dev, stream))
+    _raise("adaln_probe_clock", st)
+
+
+def adaln_probe_mark(out, slot: int, stream=None):
+    """Stream-ordered timestamp into out[slot] (int64 device tensor)."""
+    dev = _check_dev(out)
+    lib = load_library()
+    st = _on(dev, lib.adaln_probe_mark, _ptr(out), _slots(out, 1), int(slot), _stream(dev, stream))
+    _raise("adaln_probe_mark", st)
+
+
+def adaln_probe_wall_clock_khz(device=None) -> int:
+    """Rate of the wall clock the clock probes read, kHz (0 if unknown)."""
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(lib.adaln_probe_wall_clock_khz())

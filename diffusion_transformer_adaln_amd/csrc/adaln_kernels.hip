@@ -639,6 +639,16 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
   const int64_t last = rm.R - 1;
   const float inv_d = 1.0f / static_cast<float>(D);
   constexpr float n_lane = static_cast<float>(VPT * EPV);
+  // Where the next row's loads are issued.  Wide rows (8 or more vectors per
+  // lane) issue them right after the row sum, before the pass over the
+  // squared deviations: that pass is long enough to delay the request, and
+  // more so while the engine clock is low (first milliseconds of sustained
+  // load).  Video shape, D = 5120, 20 steps after 5 warm-up steps: forward
+  // 67.9 against 70.0-70.6 us, step 5,490-5,532 against 5,433-5,490 GB/s
+  // over three interleaved runs; tied at the settled clock (67.4 against
+  // 67.2 us).  Narrower rows keep the later point: D = 3072 forward 23.4
+  // against 24.3 us.
+  constexpr bool EARLY_PREFETCH = VPT >= 8;
 
   uint4 sc[VPT], sh[VPT];                   // the current sample's modulation, as stored
   int64_t cur_lo = 0, cur_hi = 0;
@@ -668,6 +678,11 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
     for (int j = 0; j < VPT; ++j) acc = E::accumulate(cur[j], acc);
     const float ml = div_count(acc, n_lane, 1.0f / n_lane);
+    if constexpr (EARLY_PREFETCH) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_row(nxt, r + active);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     float f[VPT][EPV];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) E::unpack(cur[j], f[j]);
@@ -677,13 +692,14 @@ fwd_wave_kernel(const uint4* __restrict__ x, const uint4* __restrict__ shift,
 #pragma unroll
       for (int k = 0; k < EPV; ++k) { const float d = f[j][k] - ml; sq += d * d; }
     float m = ml, s = sq;
-    // The next row's loads go out here, once this row's own pass over its
-    // registers is done, and stay in flight through the reduction and the
-    // output (measured: 67.1 us against 68.0 with them issued before the
-    // statistics, which keeps two rows per wave in flight for longer).
-    __builtin_amdgcn_sched_barrier(0);
-    load_row(nxt, r + active);
-    __builtin_amdgcn_sched_barrier(0);
+    // Otherwise the next row's loads go out here, once this row's own pass
+    // over its registers is done, and stay in flight through the reduction
+    // and the output.
+    if constexpr (!EARLY_PREFETCH) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_row(nxt, r + active);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     chan_reduce_wave(m, s, n_lane);
     const float rs = 1.0f / sqrtf(s * inv_d + eps);
     if (lane == 0) { mean[r] = m; rstd[r] = rs; }

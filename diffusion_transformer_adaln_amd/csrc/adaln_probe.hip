@@ -10,6 +10,11 @@
 // a grid of `wg_per_cu` 256-thread workgroups per compute unit.  The value
 // computed is trivial integer work, so the probes measure the memory system,
 // not the ALUs.
+//
+// The clock probe measures the engine clock itself: one wave times a chain of
+// dependent fmas against both the shader-clock cycle counter and the
+// constant-rate wall clock, so a stream of such probes beside a workload
+// shows the clock the workload ran at, moment by moment.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,7 +91,54 @@ hipError_t launch(int unroll, dim3 grid, hipStream_t s, const void* a, const voi
   return hipGetLastError();
 }
 
+// One engine-clock sample (a single wave): out[0] = wall clock at the start,
+// out[1] = shader-clock cycles of the fma chain, out[2] = its wall-clock ticks.
+__global__ void __launch_bounds__(64) clock_kernel(uint64_t* __restrict__ out, int iters) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_readcyclecounter();
+  float v = static_cast<float>(threadIdx.x) * 1e-3f;
+  for (int i = 0; i < iters; ++i) v = __builtin_fmaf(v, 0.999f, 0.5f);
+  asm volatile("" : : "v"(v));             // the chain's result is used
+  const uint64_t c1 = __builtin_readcyclecounter();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = r0;
+    out[1] = c1 - c0;
+    out[2] = r1 - r0;
+  }
+}
+
+// A stream-ordered timestamp: out[0] = wall clock when the kernel runs.
+__global__ void __launch_bounds__(64) mark_kernel(uint64_t* __restrict__ out) {
+  const uint64_t r = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) out[0] = r;
+}
+
 }  // namespace
+
+ADALN_EXPORT int64_t adaln_probe_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz > 0 ? khz : 0;
+}
+
+ADALN_EXPORT adaln_status_t adaln_probe_clock(uint64_t* out, int64_t n_slots, int64_t slot,
+                                              int iters, hipStream_t stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 7u)) return ADALN_ERR_INVALID_ARG;
+  if (n_slots < 1 || slot < 0 || slot >= n_slots) return ADALN_ERR_INVALID_ARG;
+  if (iters < 1 || iters > ADALN_PROBE_MAX_CLOCK_ITERS) return ADALN_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(clock_kernel, dim3(1), dim3(64), 0, stream, out + 3 * slot, iters);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
+
+ADALN_EXPORT adaln_status_t adaln_probe_mark(uint64_t* out, int64_t n_slots, int64_t slot,
+                                             hipStream_t stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 7u)) return ADALN_ERR_INVALID_ARG;
+  if (n_slots < 1 || slot < 0 || slot >= n_slots) return ADALN_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mark_kernel, dim3(1), dim3(64), 0, stream, out + slot);
+  return hipGetLastError() == hipSuccess ? ADALN_OK : ADALN_ERR_HIP;
+}
 
 ADALN_EXPORT size_t adaln_probe_read_out_bytes(int wg_per_cu) {
   int dev = 0, cus = 0;

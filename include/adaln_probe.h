@@ -65,6 +65,39 @@ adaln_status_t adaln_probe_stream(adaln_probe_mode_t mode, const void* a, const 
  * is out of range or the device cannot be queried). */
 size_t adaln_probe_read_out_bytes(int wg_per_cu);
 
+/*
+ * Engine-clock probes.  The kernels' rate depends on the engine clock as well
+ * as on HBM; these calls record the clock while other work runs (launch them
+ * on a second stream beside it).
+ *
+ * adaln_probe_clock -- one sample, a single wave: it runs `iters` dependent
+ * fp32 fmas and writes out[3*slot + 0] = the wall clock when it started,
+ * out[3*slot + 1] = shader-clock cycles of the fma chain, out[3*slot + 2] =
+ * wall-clock ticks of the chain.  Engine clock over that interval, in kHz:
+ * cycles / ticks * adaln_probe_wall_clock_khz().
+ *
+ *   out      device, 3 * n_slots uint64, 8-byte aligned
+ *   slot     0 <= slot < n_slots
+ *   iters    1 .. ADALN_PROBE_MAX_CLOCK_ITERS (the length of the fma chain:
+ *            a few thousand give samples of a few microseconds)
+ *
+ * adaln_probe_mark -- a stream-ordered timestamp: out[slot] = the wall clock
+ * when the mark runs (after the work enqueued before it on `stream`).
+ *   out      device, n_slots uint64, 8-byte aligned; 0 <= slot < n_slots
+ *
+ * Both: ADALN_ERR_INVALID_ARG for a violation above (nothing launched), one
+ * single-wave launch otherwise.
+ *
+ * adaln_probe_wall_clock_khz -- rate of the wall clock both read, kHz, on
+ * the current device (0 if it cannot be queried).
+ */
+#define ADALN_PROBE_MAX_CLOCK_ITERS (1 << 20)
+
+adaln_status_t adaln_probe_clock(uint64_t* out, int64_t n_slots, int64_t slot, int iters,
+                                 hipStream_t stream);
+adaln_status_t adaln_probe_mark(uint64_t* out, int64_t n_slots, int64_t slot, hipStream_t stream);
+int64_t adaln_probe_wall_clock_khz(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,8 +152,9 @@ int main(void) {
     typedef void (*fn_t)(void);
     fn_t fns[] = {(fn_t)adaln_fwd, (fn_t)adaln_bwd, (fn_t)adaln_fwd_varlen, (fn_t)adaln_bwd_varlen,
                   (fn_t)adaln_bwd_twopass, (fn_t)adaln_bwd_workspace_size, (fn_t)adaln_sched_plan,
-                  (fn_t)adaln_cost_fit, (fn_t)adaln_probe_stream};
-    for (int i = 0; i < 9; ++i) if (fns[i] == NULL) return 5;
+                  (fn_t)adaln_cost_fit, (fn_t)adaln_probe_stream, (fn_t)adaln_probe_clock,
+                  (fn_t)adaln_probe_mark, (fn_t)adaln_probe_wall_clock_khz};
+    for (size_t i = 0; i < sizeof fns / sizeof fns[0]; ++i) if (fns[i] == NULL) return 5;
   }
   puts("ok");
   return 0;
@@ -185,3 +186,17 @@ def test_probe_rejects_bad_arguments(lib):
     assert st(a=0) == bad and st(out=0) == bad
     assert st(mode=1, b=0) == bad
     assert st(a=FAKE + 8) == bad
+
+
+def test_clock_probe_rejects_bad_arguments(lib):
+    """The clock and mark probes validate before launching: a missing or
+    misaligned buffer, a slot outside [0, n_slots), a chain length outside
+    1 .. ADALN_PROBE_MAX_CLOCK_ITERS."""
+    bad = 1                      # ADALN_ERR_INVALID_ARG
+    clk = lambda out=FAKE, n=4, slot=0, it=100: lib.adaln_probe_clock(P(out), n, slot, it, None)
+    assert clk(out=0) == bad and clk(out=FAKE + 4) == bad
+    assert clk(n=0) == bad and clk(slot=-1) == bad and clk(slot=4) == bad
+    assert clk(it=0) == bad and clk(it=(1 << 20) + 1) == bad
+    mark = lambda out=FAKE, n=4, slot=0: lib.adaln_probe_mark(P(out), n, slot, None)
+    assert mark(out=0) == bad and mark(out=FAKE + 2) == bad
+    assert mark(n=0) == bad and mark(slot=-1) == bad and mark(slot=4) == bad

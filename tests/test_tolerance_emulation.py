@@ -73,7 +73,7 @@ def emulated():
     return [_emulate(*c) for c in CASES]
 
 
-def test_survey_floor_fails_correct_fp32_kernels(emulated):
+def test_floor_of_1e3_fails_correct_fp32_kernels(emulated):
     worst = max(max(_rel(r["ds"], r["ds_ref"], 1e-3), _rel(r["dh"], r["dh_ref"], 1e-3)) for r in emulated)
     print(f"floor 1e-3: worst relative error {worst:.3e}")
     assert worst > 1e-4

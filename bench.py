@@ -760,13 +760,27 @@ def clock_trace(args, runners, adaln, torch, np):
 
     m = marks.cpu().numpy()[:len(phase)].astype(np.int64)
     pr = probe.cpu().numpy().reshape(-1, 3).astype(np.int64)
+    out = {"clock_trace": {"config": args.config, "steps": args.steps, "wall_clock_khz": int(khz),
+                           "probe_iters": CLOCK_ITERS, **clock_summary(pr, m, phase, khz, np)}}
+    print(json.dumps(out), flush=True)
+
+
+def clock_summary(pr, m, phase, khz, np):
+    """Clock samples and step marks of --clock-trace, summarised.
+
+    pr: [n, 3] int64 rows (wall clock at the sample's start, shader-clock
+    cycles, wall-clock ticks; rows never written are all zero); m: the
+    marks' wall-clock stamps, one per entry of `phase` ("prime", "warmup",
+    "timed", ..., "end"), each stamped before the step it names; khz: the
+    wall clock's rate.  Times are ms from the first mark; a step lasts from
+    its mark to the next; the clock over a window is the mean of the samples
+    that start in it."""
     t0 = m[0]
-    ms = lambda ticks: ticks * 1.0 / khz                  # wall-clock ticks -> ms
     ok = pr[:, 2] > 0
-    t_s = ms(pr[ok, 0] - t0)
+    t_s = (pr[ok, 0] - t0) * 1.0 / khz
     mhz = pr[ok, 1] / pr[ok, 2] * khz / 1e3
     ph = np.array(phase)
-    t_mark = ms(m - t0)
+    t_mark = (m - t0) * 1.0 / khz
     step_us = np.diff(t_mark) * 1e3
     w_idx = np.where(ph[:-1] == "warmup")[0]
     t_idx = np.where(ph[:-1] == "timed")[0]
@@ -775,28 +789,26 @@ def clock_trace(args, runners, adaln, torch, np):
 
     def mean_in(lo, hi):
         sel = (t_s >= lo) & (t_s < hi)
-        return (round(float(mhz[sel].mean()), 1), round(float(mhz[sel].min()), 1), int(sel.sum())) if sel.any() else (None, None, 0)
+        if not sel.any():
+            return {"mean": None, "min": None, "samples": 0}
+        return {"mean": round(float(mhz[sel].mean()), 1), "min": round(float(mhz[sel].min()), 1),
+                "samples": int(sel.sum())}
 
-    keep = (t_s >= -1.0) & (t_s <= t_mark[-1] + 1.0)
-    idx = np.where(keep)[0]
-    if len(idx) > 600:
-        idx = idx[:: int(np.ceil(len(idx) / 600))]
-    wm, wmin, wn = mean_in(w_start, t_start)
-    tm, tmin, tn = mean_in(t_start, t_mark[-1])
-    out = {"clock_trace": {
-        "config": args.config, "steps": args.steps, "warmup": int(len(w_idx)),
-        "wall_clock_khz": int(khz), "probe_iters": CLOCK_ITERS,
-        "probe_us": round(float(np.median(pr[ok, 2])) / khz * 1e3, 2),
+    keep = np.where((t_s >= -1.0) & (t_s <= t_mark[-1] + 1.0))[0]
+    if len(keep) > 600:
+        keep = keep[:: int(np.ceil(len(keep) / 600))]
+    return {
+        "warmup": int(len(w_idx)),
+        "probe_us": round(float(np.median(pr[ok, 2])) / khz * 1e3, 2) if ok.any() else None,
         "idle_mhz": round(float(np.median(mhz[t_s < 0])), 1) if (t_s < 0).any() else None,
         "prime_ms": round(float(w_start), 3),
-        "warmup_mhz": {"mean": wm, "min": wmin, "samples": wn},
-        "timed_mhz": {"mean": tm, "min": tmin, "samples": tn},
+        "warmup_mhz": mean_in(w_start, t_start),
+        "timed_mhz": mean_in(t_start, t_mark[-1]),
         "timed_start_ms": round(float(t_start), 3), "end_ms": round(float(t_mark[-1]), 3),
         "timed_step_us": [round(float(v), 1) for v in step_us[t_idx]],
         "warmup_step_us": [round(float(v), 1) for v in step_us[w_idx]][:50],
-        "samples_ms_mhz": [[round(float(t_s[i]), 3), round(float(mhz[i]), 0)] for i in idx],
-    }}
-    print(json.dumps(out), flush=True)
+        "samples_ms_mhz": [[round(float(t_s[i]), 3), round(float(mhz[i]), 0)] for i in keep],
+    }
 
 
 def read_traffic(path, config):

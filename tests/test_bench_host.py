@@ -40,3 +40,34 @@ def test_more_than_one_gpu_is_refused_with_a_reason():
                          text=True, timeout=120)
     assert run.returncode != 0
     assert "exactly one GPU" in run.stdout + run.stderr
+
+
+def test_clock_summary_splits_the_schedule_and_converts_cycles():
+    """--clock-trace's summary on a synthetic trace: a 100 MHz wall clock,
+    marks for priming, two warm-up steps and three timed steps, samples at
+    2.4 GHz before the schedule, 2.0 GHz over the warm-up and 1.5 GHz over
+    the timed steps, and rows never written (all zero) ignored."""
+    import numpy as np
+
+    import bench
+
+    khz = 100_000                                  # ticks per ms
+    m0 = 10_000_000
+    stamps_ms = [0.0, 0.5, 0.7, 0.9, 1.1, 1.3, 1.5]  # prime, warm-up x2, timed x3, end
+    phase = ["prime", "warmup", "warmup", "timed", "timed", "timed", "end"]
+    m = np.array([m0 + int(t * khz) for t in stamps_ms], dtype=np.int64)
+
+    def sample(t_ms, ghz, dur_ms=0.05):
+        ticks = int(dur_ms * khz)
+        return [m0 + int(t_ms * khz), int(ghz * 1e6 * dur_ms), ticks]   # cycles = GHz * 1e9 * s
+
+    rows = [sample(-0.2, 2.4), sample(-0.1, 2.4), sample(0.55, 2.0), sample(0.8, 2.0),
+            sample(0.95, 1.5), sample(1.2, 1.5), sample(1.4, 1.5), [0, 0, 0], [0, 0, 0]]
+    pr = np.array(rows, dtype=np.int64)
+    s = bench.clock_summary(pr, m, phase, khz, np)
+    assert s["warmup"] == 2 and s["prime_ms"] == 0.5 and s["timed_start_ms"] == 0.9 and s["end_ms"] == 1.5
+    assert s["idle_mhz"] == 2400.0
+    assert s["warmup_mhz"] == {"mean": 2000.0, "min": 2000.0, "samples": 2}
+    assert s["timed_mhz"] == {"mean": 1500.0, "min": 1500.0, "samples": 3}
+    assert s["timed_step_us"] == [200.0, 200.0, 200.0] and s["warmup_step_us"] == [200.0, 200.0]
+    assert s["probe_us"] == 50.0 and len(s["samples_ms_mhz"]) == 7

@@ -140,7 +140,7 @@ def assert_norm(got, ref, tol, what):
 
 
 def assert_rel_floored(got, ref, tol, what, extra=None):
-    """Per sample row: |got-ref| <= tol * max(|ref|, 1e-2 * rms(ref)) + extra.
+    """Per sample row: |got-ref| <= tol * max(|ref|, REL_FLOOR * rms(ref)) + extra.
 
     Returns the worst ratio of error to bound scaled by tol (the plain relative
     error when extra is None)."""

@@ -6,7 +6,6 @@ loads that copy as a separate module on the CPU, and requires at least one pin
 to fail on it.  The real oracle is never modified.
 """
 
-import importlib.util
 import os
 import sys
 import types

@@ -163,7 +163,7 @@ adaln_status_t bwd_common(const void* dy, const void* x, const void* scale, cons
                       {offsets, offsets ? (B + 1) * 8 : 0}};
   if (any_alias(outs, 4, ins, 6)) return ADALN_ERR_ALIASING;
 
-  const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true, offsets != nullptr);
+  const adaln::VecPlan vp = adaln::plan_vec(dtype, D, true, offsets != nullptr, B);
   const bool vec = vp.ok && aligned16(dy) && aligned16(x) && aligned16(dx) && aligned16(scale);
   const bool twopass = mode == BwdMode::kTwoPass;
   if (twopass && !vec) return ADALN_ERR_UNSUPPORTED_SHAPE;

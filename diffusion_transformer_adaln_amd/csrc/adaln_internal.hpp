@@ -88,9 +88,18 @@ constexpr int BWD_MAX_VPT = 4;
 // finish from 10.0 to 6.4 us on the video shape against a tile-major layout).
 constexpr int PCOLS = 16;
 
+// Packed batches of at most this many samples are tiled like dense ones (two
+// tiles per CU), and the backward kernels rebuild their tile table per wave
+// (one sample per lane) instead of reading one written by a prologue launch.
+constexpr int64_t PACKED_FEW_SAMPLES = 64;
+
+// Backward tiles per CU: 2 for dense batches and packed batches of few
+// samples, 4 for packed batches of more samples.
+int bwd_tiles_per_cu(bool varlen, int64_t B);
+
 // Vector plan for the forward (backward = false) or backward kernels; varlen
-// selects the packed backward's tiling (more tiles per CU).
-VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen = false);
+// and B (samples) select the backward's tiling.
+VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen = false, int64_t B = 1);
 
 // Dynamic LDS bytes of a vectorised launch with plan p.
 size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward);
@@ -115,8 +124,9 @@ hipError_t launch_bwd_twopass(int dtype, const void* dy, const void* x, const vo
                               const VecPlan& vp, const Tiling& tl, float* partial,
                               hipStream_t stream, void* dx, void* dscale, void* dshift);
 
-// Rows per backward tile for R rows on a device with num_cu compute units.
-int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen);
+// Rows per backward tile for R rows in B samples on a device with num_cu
+// compute units.
+int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen);
 
 // Bytes of workspace for the backward (tile table + partial sums).
 size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);

@@ -344,14 +344,15 @@ __device__ __forceinline__ int64_t sample_of_row(const RowMap& rm, int64_t row) 
   return lo;
 }
 
-// Packed batches of at most VARLEN_WAVE_MAX_B samples need no tile table in
-// memory (and no prologue launch): any wave rebuilds it from the offsets.
+// Packed batches of at most PACKED_FEW_SAMPLES (64) samples need no tile
+// table in memory (and no prologue launch): any wave rebuilds it from the
+// offsets.
 // Lane i holds sample i's tile count (ceil of its clamped row count over
 // tile_rows); an inclusive prefix sum over the wave gives every sample's tile
 // range [excl, incl), both capped at tiles_alloc exactly as the prologue caps
 // the table it writes, so both ways number the tiles identically.  Every lane
 // of the wave must take part.
-constexpr int VARLEN_WAVE_MAX_B = 64;
+static_assert(PACKED_FEW_SAMPLES <= 64, "one sample per lane of a wave");
 
 struct WaveTiles {
   int64_t excl, incl;   // this lane's sample: tiles [excl, incl)
@@ -1683,12 +1684,12 @@ static hipError_t finish_launch(const RowMap& rm, int64_t D, const Tiling& tl,
                                 const float* partial, hipStream_t stream, void* dscale,
                                 void* dshift);
 
-// The packed batch's tile table: batches of at most VARLEN_WAVE_MAX_B
+// The packed batch's tile table: batches of at most PACKED_FEW_SAMPLES
 // samples rebuild it wave by wave inside the kernels (tile_start = nullptr
 // tells them so), larger ones get it from the prologue kernel.
 static hipError_t varlen_tile_table(const RowMap& rm, Tiling& tl, hipStream_t stream) {
   if (rm.offsets == nullptr) return hipSuccess;
-  if (rm.B <= VARLEN_WAVE_MAX_B) {
+  if (rm.B <= PACKED_FEW_SAMPLES) {
     tl.tile_start = nullptr;
     return hipSuccess;
   }

@@ -28,11 +28,17 @@ size_t vec_lds_bytes(const VecPlan& p, int64_t D, bool backward) {
 // call, video shape: one 147 us, two 102, three 128, four 142; MMDiT 42.9,
 // 37.9, 42.8, 44.1; DiT 24.2, 20.9, 26.1, 24.7).
 constexpr int BWD_TILES_PER_CU = 2;
-// Packed batches mix short and long samples, so their tiles vary in length;
-// four tiles per CU lets the workgroup dispatcher even out the load (mixed
-// 256..32760-row samples at D = 3072, backward call: 946 us at two per CU,
-// 914 at three, 862 at four, 899 at six, 872 at eight).
+// Packed batches of many samples (more than PACKED_FEW_SAMPLES) mix short and
+// long samples, so their tiles vary in length; four tiles per CU lets the
+// workgroup dispatcher even out the load (mixed 256..32760-row samples at
+// D = 3072, backward call: 946 us at two per CU, 914 at three, 862 at four,
+// 899 at six, 872 at eight).  Packed batches of few samples are tiled like
+// dense ones (two per CU, see bwd_tile_rows).
 constexpr int BWD_VARLEN_TILES_PER_CU = 4;
+
+int bwd_tiles_per_cu(bool varlen, int64_t B) {
+  return varlen && B > PACKED_FEW_SAMPLES ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU;
+}
 
 // Row layout for a D-wide row: VPT vectors per lane over LPR = V/VPT lanes,
 // LPR a multiple of 16.  Measured on MI355X (video shape, D = 5120 bf16):
@@ -44,7 +50,7 @@ constexpr int BWD_VARLEN_TILES_PER_CU = 4;
 //            accumulators, the modulation row and the row data small enough
 //            for four waves per SIMD.
 // Ties prefer rows that cover whole waves (no partial-wave reductions).
-VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen) {
+VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen, int64_t B) {
   VecPlan best{false, 0, 0, 0, 1};
   const int max_vpt = backward ? BWD_MAX_VPT : FWD_MAX_VPT;
   const int epv = dtype == BF16 ? 8 : 4;
@@ -69,10 +75,12 @@ VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen) {
     // CU's tiles, one row each, would hold less than BWD_MIN_CU_BYTES of dy
     // and x in flight.  Dense D = 3072 bf16 (two tiles of 12 KB rows): MMDiT's
     // 8,192-row image stream 42.6 -> 38.0 us per backward, its 1,024-row text
-    // stream 17.9 -> 15.1 us with 4-row tiles (below).  Packed D = 3072 (four
-    // tiles, 48 KB) was 3% slower with two slots; dense D = 5120 (40 KB) too.
+    // stream 17.9 -> 15.1 us with 4-row tiles (below); packed batches of few
+    // samples take the same rule.  Packed batches of many samples at
+    // D = 3072 (four tiles, 48 KB) were 3% slower with two slots; dense
+    // D = 5120 (40 KB) too.
     const int64_t esize = dtype == BF16 ? 2 : 4;
-    const int64_t tiles_per_cu = varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU;
+    const int64_t tiles_per_cu = bwd_tiles_per_cu(varlen, B);
     if (backward && nt == p.lpr && tiles_per_cu * 2 * D * esize < BWD_MIN_CU_BYTES &&
         2 * nt <= VEC_MAX_NT)
       nt *= 2;
@@ -90,10 +98,19 @@ VecPlan plan_vec(int dtype, int64_t D, bool backward, bool varlen) {
 // keeps several rows in flight (MMDiT's 1,024-row text stream at D = 3072:
 // 15.1 us per backward with 4-row tiles, 18.3 with 2, 16.4 with 8).
 constexpr int64_t BWD_MIN_TILE_ROWS = 4;
-int64_t bwd_tile_rows(int64_t R, int num_cu, bool varlen) {
-  const int64_t target =
-      static_cast<int64_t>(num_cu) * (varlen ? BWD_VARLEN_TILES_PER_CU : BWD_TILES_PER_CU);
-  const int64_t rows = R <= 0 ? 1 : (R + target - 1) / target;
+//
+// A packed batch of few samples ends each sample in a partial tile, so it has
+// up to B tiles more than R / tile_rows; its tiles are sized for target - B
+// of them, which keeps the count at or below target (two per CU).  One tile
+// too many puts a third equal workgroup on some CU, which then finishes last:
+// four packed samples of D = 3072 summing to 9,216 rows, fwd+bwd step 80.1 us
+// with 514 tiles of 18 rows against 67.0 us for a split into exactly 512, and
+// 67.5 us with the tiles sized this way (73.1 at four tiles per CU; the
+// one-sample 18,900-row batch at D = 5120: 173.9 against 199.8 us).
+int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen) {
+  const int64_t target = static_cast<int64_t>(num_cu) * bwd_tiles_per_cu(varlen, B);
+  const int64_t slots = varlen && B <= PACKED_FEW_SAMPLES && target > B ? target - B : target;
+  const int64_t rows = R <= 0 ? 1 : (R + slots - 1) / slots;
   return rows < BWD_MIN_TILE_ROWS ? BWD_MIN_TILE_ROWS : rows;
 }
 
@@ -102,7 +119,7 @@ static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255);
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense) {
   WorkspaceLayout w{};
-  w.tile_rows = bwd_tile_rows(R, num_cu, varlen);
+  w.tile_rows = bwd_tile_rows(R, B, num_cu, varlen);
   const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;   // tiles of any row split
   w.tiles_alloc = bound;
   w.tiles_max = varlen ? bound : B * ((N_dense + w.tile_rows - 1) / w.tile_rows);

@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <limits>
+#include <algorithm>
 #include <vector>
 
 #include "adaln.h"
@@ -296,9 +297,9 @@ static void test_plans() {
   for (int dt : {adaln::F32, adaln::BF16}) {
     const int64_t epv = dt == adaln::BF16 ? 8 : 4;
     for (int64_t D = 1; D <= ADALN_MAX_D; ++D) {
-      for (int dir = 0; dir < 3; ++dir) {   // forward, dense backward, packed backward
+      for (int dir = 0; dir < 4; ++dir) {   // forward, dense backward, packed backward (few, many samples)
         const bool bwd = dir > 0;
-        const adaln::VecPlan p = adaln::plan_vec(dt, D, bwd, dir == 2);
+        const adaln::VecPlan p = adaln::plan_vec(dt, D, bwd, dir >= 2, dir == 3 ? 277 : 4);
         if (!p.ok) continue;   // the general kernels take these widths
         const int64_t V = D / epv;
         const bool shape_ok = p.vpt >= 1 && p.vpt <= (bwd ? adaln::BWD_MAX_VPT : adaln::FWD_MAX_VPT) &&
@@ -316,8 +317,9 @@ static void test_plans() {
   const struct { int dt; int64_t D; } want[] = {{adaln::F32, 128}, {adaln::BF16, 1152}, {adaln::BF16, 3072},
                                                {adaln::BF16, 5120}, {adaln::BF16, 16384}, {adaln::F32, 4096}};
   for (const auto& w : want)
-    for (int dir = 0; dir < 3; ++dir)
-      EXPECT(adaln::plan_vec(w.dt, w.D, dir > 0, dir == 2).ok, "no vector plan for dtype %d D %lld dir %d", w.dt,
+    for (int dir = 0; dir < 4; ++dir)
+      EXPECT(adaln::plan_vec(w.dt, w.D, dir > 0, dir >= 2, dir == 3 ? 277 : 4).ok,
+             "no vector plan for dtype %d D %lld dir %d", w.dt,
              (long long)w.D, dir);
   const int64_t Bs[] = {1, 2, 3, 8, 277};
   const int64_t Ns[] = {0, 1, 2, 3, 5, 64, 100, 512, 1023, 4096, 18900, 64000};
@@ -442,8 +444,36 @@ static void test_wave_tile_lookup() {
   }
 }
 
+// Packed batches of few samples are tiled so that their tile count stays at
+// or below two per CU whatever the split of the rows into samples (one tile
+// more puts a third equal workgroup on some CU); batches of more samples keep
+// four tiles per CU.
+static void test_few_sample_tile_bound() {
+  uint64_t seed = 777;
+  auto next = [&seed]() { seed = seed * 6364136223846793005ull + 1442695040888963407ull; return seed >> 33; };
+  for (int cus : {80, 256, 304}) {
+    for (int B : {1, 2, 3, 4, 9, 16, 33, 64}) {
+      for (int rep = 0; rep < 40; ++rep) {
+        std::vector<int64_t> n(B);
+        int64_t R = 0;
+        for (int b = 0; b < B; ++b) { n[b] = static_cast<int64_t>(next() % (rep % 2 ? 9000 : 700)); R += n[b]; }
+        const adaln::WorkspaceLayout w = adaln::bwd_workspace_layout(B, R, 3072, cus, true, 0);
+        int64_t tiles = 0;
+        for (int b = 0; b < B; ++b) tiles += (n[b] + w.tile_rows - 1) / w.tile_rows;
+        const bool ok = tiles <= std::max<int64_t>(2 * cus, B) && tiles <= w.tiles_alloc;
+        EXPECT(ok, "few-sample packed batch: %lld tiles on %d CUs (B %d, R %lld, tile_rows %lld)",
+               (long long)tiles, cus, B, (long long)R, (long long)w.tile_rows);
+      }
+    }
+  }
+  EXPECT(adaln::bwd_tiles_per_cu(false, 1000) == 2 && adaln::bwd_tiles_per_cu(true, 64) == 2 &&
+             adaln::bwd_tiles_per_cu(true, 65) == 4,
+         "tiles per CU: dense 2, packed up to 64 samples 2, more 4");
+}
+
 int main() {
   test_offset_clamp();
+  test_few_sample_tile_bound();
   test_wave_tile_lookup();
   test_plans();
   test_forward();

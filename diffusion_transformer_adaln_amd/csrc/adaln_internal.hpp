@@ -124,9 +124,9 @@ hipError_t launch_bwd_twopass(int dtype, const void* dy, const void* x, const vo
                               const VecPlan& vp, const Tiling& tl, float* partial,
                               hipStream_t stream, void* dx, void* dscale, void* dshift);
 
-// Rows per backward tile for R rows in B samples on a device with num_cu
-// compute units.
-int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen);
+// Rows per backward tile for R rows in B samples (of N_dense rows each for a
+// dense batch) on a device with num_cu compute units.
+int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen, int64_t N_dense);
 
 // Bytes of workspace for the backward (tile table + partial sums).
 size_t bwd_workspace_bytes(int64_t B, int64_t R, int64_t D, int num_cu);

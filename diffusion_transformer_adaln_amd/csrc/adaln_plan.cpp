@@ -107,10 +107,20 @@ constexpr int64_t BWD_MIN_TILE_ROWS = 4;
 // with 514 tiles of 18 rows against 67.0 us for a split into exactly 512, and
 // 67.5 us with the tiles sized this way (73.1 at four tiles per CU; the
 // one-sample 18,900-row batch at D = 5120: 173.9 against 199.8 us).
-int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen) {
+//
+// A dense batch of B samples of N rows has B * ceil(N / tile_rows) tiles,
+// which can exceed the target by up to B - 1 (B = 3, N = 4096: 513 tiles of
+// 24 rows); its tiles are lengthened until at most target / B fit in a
+// sample, which leaves every batch that already fits as it was.
+int64_t bwd_tile_rows(int64_t R, int64_t B, int num_cu, bool varlen, int64_t N_dense) {
   const int64_t target = static_cast<int64_t>(num_cu) * bwd_tiles_per_cu(varlen, B);
   const int64_t slots = varlen && B <= PACKED_FEW_SAMPLES && target > B ? target - B : target;
-  const int64_t rows = R <= 0 ? 1 : (R + slots - 1) / slots;
+  int64_t rows = R <= 0 ? 1 : (R + slots - 1) / slots;
+  if (!varlen && N_dense > 0 && B > 0 && target / B >= 1) {
+    const int64_t per_sample = target / B;
+    const int64_t fit = (N_dense + per_sample - 1) / per_sample;
+    if (fit > rows) rows = fit;
+  }
   return rows < BWD_MIN_TILE_ROWS ? BWD_MIN_TILE_ROWS : rows;
 }
 
@@ -119,7 +129,7 @@ static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255);
 WorkspaceLayout bwd_workspace_layout(int64_t B, int64_t R, int64_t D, int num_cu, bool varlen,
                                      int64_t N_dense) {
   WorkspaceLayout w{};
-  w.tile_rows = bwd_tile_rows(R, B, num_cu, varlen);
+  w.tile_rows = bwd_tile_rows(R, B, num_cu, varlen, N_dense);
   const int64_t bound = (R + w.tile_rows - 1) / w.tile_rows + B;   // tiles of any row split
   w.tiles_alloc = bound;
   w.tiles_max = varlen ? bound : B * ((N_dense + w.tile_rows - 1) / w.tile_rows);

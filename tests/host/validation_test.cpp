@@ -466,6 +466,16 @@ static void test_few_sample_tile_bound() {
       }
     }
   }
+  // dense batches: at most two tiles per CU whenever B allows it
+  for (int cus : {80, 256, 304})
+    for (int64_t B : {1, 2, 3, 5, 6, 7, 8, 100, 511, 600})
+      for (int64_t N : {1, 5, 255, 777, 1000, 2000, 3000, 4096, 4097, 18900, 64000}) {
+        const adaln::WorkspaceLayout w = adaln::bwd_workspace_layout(B, B * N, 3072, cus, false, N);
+        const int64_t tiles = B * ((N + w.tile_rows - 1) / w.tile_rows);
+        EXPECT(tiles == w.tiles_max && tiles <= std::max<int64_t>(2 * cus, B),
+               "dense batch B %lld N %lld on %d CUs: %lld tiles of %lld rows", (long long)B, (long long)N, cus,
+               (long long)tiles, (long long)w.tile_rows);
+      }
   EXPECT(adaln::bwd_tiles_per_cu(false, 1000) == 2 && adaln::bwd_tiles_per_cu(true, 64) == 2 &&
              adaln::bwd_tiles_per_cu(true, 65) == 4,
          "tiles per CU: dense 2, packed up to 64 samples 2, more 4");

@@ -95,6 +95,9 @@ SHAPES = [
     # (64 lanes x 1..10 vectors), with ragged and multi-sample batches
     ("bf16", 512, [33, 2]), ("bf16", 1536, [40]), ("bf16", 2560, [50, 3]), ("bf16", 3584, [33]),
     ("bf16", 4608, [7, 70]), ("f32", 1280, [40]), ("f32", 1792, [9, 9]), ("f32", 2560, [21]),
+    # dense batches whose plain tiling would overflow two tiles per CU (3 x 4096 rows: 513
+    # tiles of 24 rows), so the planner lengthens the tiles; packed twins take the few-sample rule
+    ("bf16", 3072, [4096] * 3), ("f32", 1280, [4096] * 3),
 ]
 
 
